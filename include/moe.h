@@ -1,0 +1,171 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse mixture-of-experts layer.
+ *
+ * One layer computes, for T tokens of hidden state x [T x H]:
+ *   1. router logits l = x Wr^T + b                     (Wr [E x H] bf16, b [E] fp32)
+ *   2. per token, the top-k experts by (logit descending, lower id first on
+ *      equal logits), with weights w_j = softmax over the k selected logits
+ *      (the renormalised softmax over all E experts)
+ *   3. the (token, expert) pairs grouped by expert with a stable counting sort
+ *   4. per pair, the expert FFN  D (silu(G x) * (U x))  over block-quantised
+ *      weights (G, U [F x H], D [H x F])
+ *   5. y_t = sum_j w_tj * FFN_{e_tj}(x_t)  (+ the shared expert with weight 1)
+ *
+ * What the pages fix and what they leave open:
+ *  - Sparse top-k routing over hundreds of experts, a shared expert and fused
+ *    gate/up/down expert tensors: page "Strata 改源码去跑 DeepSeek V4 Flash？",
+ *    section 二 (GGUF table: 256 routed + 1 shared, 6 active, FF 2048,
+ *    hidden 4096, router bias); the teardown page "Strata 引擎深度拆解",
+ *    section 二 (48 layers x 512 experts, 10 active per token).
+ *  - E and k are runtime values and a wrong expert width is rejected, not
+ *    reinterpreted: the first page, section 三 (items 2 and 4).
+ *  - The problem statement "hidden state in, routed top-k experts, weighted
+ *    FFN sum out" at fixed weights: the first page, section 六.
+ *  - The routing function, the activation and the combine rule are not on
+ *    the pages.  Readings used: softmax top-k with renormalisation, bias added
+ *    to the logits before selection and softmax, SwiGLU, shared expert added
+ *    with weight 1.
+ *
+ * Expert byte format accepted by moe_load_experts ("canonical blocks"): an
+ * expert is G rows, then U rows, then D rows; every row is a sequence of
+ * blocks of 32 consecutive weights along its input dimension; a block is an
+ * fp16 scale d (little-endian) followed by the codes:
+ *   MOE_Q4B32  18 bytes/block, weight j in byte j>>1 (low nibble first), w = d*(q-8)
+ *   MOE_Q2B32  10 bytes/block, weight j in byte j>>2 at bit 2*(j&3),     w = d*(q-2)
+ * so one expert is 3*H*F/32 blocks (q4b32 at H=4096, F=2048: 14,155,776 bytes).
+ *
+ * Conventions for every call:
+ *  - Device pointers are plain device addresses on the context's device,
+ *    16-byte aligned, contiguous, owned by the caller and alive until the
+ *    work queued on the passed stream has completed.  Host pointers are
+ *    read before the call returns.
+ *  - Calls are ordered on the HIP stream passed in (NULL = the null stream)
+ *    and never synchronise the device implicitly, except moe_load_experts
+ *    and moe_destroy, which are synchronous.
+ *  - Validation runs before any launch: a call that returns an error has
+ *    queued no work and changed no state.  A HIP runtime failure returns
+ *    MOE_EHIP and poisons the context (every later call returns MOE_ESTATE).
+ *  - No C++ exception crosses this interface.  moe_last_error() returns a
+ *    thread-local description of the last non-OK status of this thread.
+ *  - A context must not be used from two host threads at once.  Calls on one
+ *    context share its scratch memory: queue them on one stream.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1, /* bad argument: shape, format, size, alignment, NULL pointer */
+    MOE_ENOMEM = -2, /* device or pinned host allocation failed */
+    MOE_EHIP = -3,   /* a HIP runtime call failed; the context is poisoned */
+    MOE_ESTATE = -4, /* layer used before it was loaded, or poisoned context */
+    MOE_ERANGE = -5  /* T larger than the context's max_tokens */
+} moe_status;
+
+typedef enum { MOE_Q4B32 = 1, MOE_Q2B32 = 2 } moe_quant;
+
+/* Layer geometry, fixed for the lifetime of a context (E and k are runtime
+ * values, as the pages' engine reads them from the model file).
+ *   hidden, ffn : H and F, positive multiples of 32
+ *   n_experts   : E routed experts, 1..1024
+ *   n_shared    : 0 or 1 always-on shared expert (expert index E)
+ *   top_k       : k in [1, min(E, 16)]
+ *   n_layers    : L >= 1; every layer has its own router and experts
+ *   quant       : MOE_Q4B32 or MOE_Q2B32
+ *   max_tokens  : largest T accepted by moe_route/moe_forward (1..65536);
+ *                 scratch memory is sized for it
+ *   device      : HIP device ordinal */
+typedef struct {
+    int32_t abi_version; /* MOE_ABI_VERSION */
+    int32_t hidden, ffn, n_experts, n_shared, top_k, n_layers, quant, max_tokens, device;
+} moe_config;
+
+/* One upload of weights for one layer (host memory, read synchronously).
+ *   router_w    : [E x H] bf16 bit patterns, or NULL to leave the router as is
+ *   router_bias : [E] fp32, or NULL (a router upload with NULL bias sets b = 0)
+ *   experts     : expert_count experts in canonical blocks, experts
+ *                 [expert_begin, expert_begin + expert_count); index E is the
+ *                 shared expert.  NULL with expert_count = 0 uploads none.
+ *   experts_bytes must equal expert_count * 3*H*F/32 * (18 or 10). */
+typedef struct {
+    int32_t layer, expert_begin, expert_count;
+    const uint16_t* router_w;
+    const float* router_bias;
+    const uint8_t* experts;
+    size_t experts_bytes;
+} moe_layer_weights;
+
+#define MOE_FWD_RESIDUAL 1 /* x_{l+1} = bf16(fp32(x_l) + y_l); else x_{l+1} = bf16(y_l) */
+
+/* One forward pass through layers [layer_begin, layer_begin + layer_count).
+ *   x      : [T x H] bf16, device, input of the first layer
+ *   y      : [T x H] bf16, device, output of the last layer (the residual
+ *            sum when MOE_FWD_RESIDUAL is set); may not alias x
+ *   trace_x  : NULL or [layer_count x T x H] bf16, each layer's input
+ *   trace_ids: NULL or [layer_count x T x k] int32, each layer's routing
+ *   trace_w  : NULL or [layer_count x T x k] fp32, each layer's weights */
+typedef struct {
+    int32_t layer_begin, layer_count, T, flags;
+    const void* x;
+    void* y;
+    void* trace_x;
+    int32_t* trace_ids;
+    float* trace_w;
+} moe_fwd_args;
+
+typedef struct moe_ctx moe_ctx;
+
+/* Allocate the context on cfg->device: one device arena holding every
+ * expert of every layer (L x (E+S) slots), the routers, and scratch sized by
+ * max_tokens.  Returns MOE_EINVAL for a bad geometry, MOE_ENOMEM when the
+ * arena does not fit (nothing stays allocated).  *out is set only on MOE_OK. */
+moe_status moe_create(const moe_config* cfg, moe_ctx** out);
+
+/* Upload router weights and/or experts of one layer.  The canonical blocks are
+ * copied through a bounded pinned staging buffer and re-laid-out on the
+ * device into the context's slot format.  Returns when the host memory is no
+ * longer read; the device work is ordered before any later call on the
+ * context.  MOE_EINVAL on a wrong byte count, range or layer. */
+moe_status moe_load_experts(moe_ctx* ctx, const moe_layer_weights* w);
+
+/* Routing of one layer (steps 1-3 above) for T tokens of x [T x H] bf16.
+ *   ids     : [T x k] int32, device; expert ids per token in selection order
+ *   w       : [T x k] fp32, device; renormalised weights, same order, sum 1
+ *   offsets : NULL or [E+1] int32, device; exclusive prefix sum of the number
+ *             of pairs per expert (offsets[E] = T*k)
+ *   perm    : NULL or [T*k] int32, device; pair indices i = t*k + j grouped by
+ *             expert id, ascending i inside a group (stable)
+ * MOE_ESTATE if the layer's router is not loaded; T = 0 is a no-op. */
+moe_status moe_route(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, int32_t* ids, float* w,
+                     int32_t* offsets, int32_t* perm, void* hip_stream);
+
+/* Whole layers (steps 1-5) for T tokens; see moe_fwd_args.  MOE_ESTATE if a
+ * layer's router or any of its experts is not loaded, MOE_ERANGE if
+ * T > max_tokens, MOE_OK and no work for T = 0. */
+moe_status moe_forward(moe_ctx* ctx, const moe_fwd_args* args, void* hip_stream);
+
+/* Wait for the context's work, free everything it owns.  NULL is a no-op. */
+moe_status moe_destroy(moe_ctx* ctx);
+
+/* Thread-local text of the last non-OK status returned to this thread. */
+const char* moe_last_error(void);
+
+/* Canonical bytes of one expert (3*H*F/32 blocks), or -1 for a bad shape. */
+int64_t moe_expert_bytes(int32_t hidden, int32_t ffn, int32_t quant);
+
+/* Device bytes the context holds: expert arena, routers and scratch. */
+moe_status moe_memory_bytes(const moe_ctx* ctx, uint64_t* arena_bytes, uint64_t* scratch_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,397 @@
+// Host runtime behind include/moe.h: configuration checks, the resident expert
+// slot table, scratch memory, weight upload and the per-layer launch plan.
+//
+// Every expert of every layer lives in one device arena (the slot table): with
+// 288 GB of HBM on one MI355X the pages' VRAM/RAM/SSD expert waterfall
+// (teardown page "Strata 引擎深度拆解", section 二.1) is not needed, and no
+// expert is ever fetched over PCIe during a forward pass.  The geometry is a
+// runtime value checked once at creation; a wrong expert byte count is
+// rejected, in the spirit of the width check quoted on "Strata 改源码去跑
+// DeepSeek V4 Flash？", section 三 item 4.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status fail(moe_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+constexpr size_t kStagingBytes = 64ull << 20;  // bounded host staging for weight upload
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+struct moe_ctx {
+    moe_config cfg{};
+    Geom g{};
+    bool poisoned = false;
+    uint8_t* arena = nullptr;      // L x (E+S) expert slots
+    uint16_t* routers = nullptr;   // L x E x H bf16
+    float* biases = nullptr;       // L x E
+    std::vector<uint8_t> router_loaded;
+    std::vector<uint8_t> expert_loaded;
+    // scratch
+    uint8_t* scratch = nullptr;
+    size_t scratch_bytes = 0;
+    RouteBufs rb{};
+    DecodeBufs db{};
+    uint16_t* xbuf[2] = {nullptr, nullptr};
+    int maxA = 0;
+    int decode_T = 0;
+    // upload
+    hipStream_t load_stream = nullptr;
+    uint8_t* host_stage[2] = {nullptr, nullptr};
+    uint8_t* dev_stage[2] = {nullptr, nullptr};
+    hipEvent_t stage_done[2] = {nullptr, nullptr};
+    uint64_t arena_bytes = 0;
+};
+
+namespace {
+
+moe_status hip_fail(moe_ctx* c, hipError_t e, const char* what) {
+    if (c) c->poisoned = true;
+    return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(ctx, call)                                   \
+    do {                                                     \
+        hipError_t e_ = (call);                              \
+        if (e_ != hipSuccess) return hip_fail(ctx, e_, #call); \
+    } while (0)
+
+void free_ctx(moe_ctx* c) {
+    if (!c) return;
+    if (c->load_stream) hipStreamSynchronize(c->load_stream);
+    for (int i = 0; i < 2; ++i) {
+        if (c->host_stage[i]) hipHostFree(c->host_stage[i]);
+        if (c->dev_stage[i]) hipFree(c->dev_stage[i]);
+        if (c->stage_done[i]) hipEventDestroy(c->stage_done[i]);
+    }
+    if (c->load_stream) hipStreamDestroy(c->load_stream);
+    if (c->scratch) hipFree(c->scratch);
+    if (c->biases) hipFree(c->biases);
+    if (c->routers) hipFree(c->routers);
+    if (c->arena) hipFree(c->arena);
+    delete c;
+}
+
+moe_status check_config(const moe_config* cfg) {
+    if (!cfg) return fail(MOE_EINVAL, "config is NULL");
+    if (cfg->abi_version != MOE_ABI_VERSION)
+        return fail(MOE_EINVAL, "abi_version %d, library is %d", cfg->abi_version, MOE_ABI_VERSION);
+    if (cfg->hidden <= 0 || cfg->hidden % 32 || cfg->ffn <= 0 || cfg->ffn % 32)
+        return fail(MOE_EINVAL, "hidden (%d) and ffn (%d) must be positive multiples of 32", cfg->hidden, cfg->ffn);
+    if (cfg->hidden > 65536 || cfg->ffn > 65536) return fail(MOE_EINVAL, "hidden/ffn above 65536");
+    if (cfg->n_experts < 1 || cfg->n_experts > kMaxExperts)
+        return fail(MOE_EINVAL, "n_experts %d outside [1, %d]", cfg->n_experts, kMaxExperts);
+    if (cfg->n_shared != 0 && cfg->n_shared != 1) return fail(MOE_EINVAL, "n_shared must be 0 or 1");
+    if (cfg->top_k < 1 || cfg->top_k > std::min(cfg->n_experts, kMaxTopK))
+        return fail(MOE_EINVAL, "top_k %d outside [1, min(E, %d)]", cfg->top_k, kMaxTopK);
+    if (cfg->n_layers < 1 || cfg->n_layers > 4096) return fail(MOE_EINVAL, "n_layers %d outside [1, 4096]", cfg->n_layers);
+    if (cfg->quant != MOE_Q4B32 && cfg->quant != MOE_Q2B32) return fail(MOE_EINVAL, "unknown quant %d", cfg->quant);
+    if (cfg->max_tokens < 1 || cfg->max_tokens > 65536)
+        return fail(MOE_EINVAL, "max_tokens %d outside [1, 65536]", cfg->max_tokens);
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device < 0 || cfg->device >= ndev)
+        return fail(MOE_EINVAL, "device %d not present (%d devices)", cfg->device, ndev);
+    return MOE_OK;
+}
+
+// Carve the scratch arena.
+struct Carver {
+    size_t off = 0;
+    template <class T> size_t take(size_t count) {
+        off = (off + 255) / 256 * 256;
+        size_t o = off;
+        off += count * sizeof(T);
+        return o;
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int64_t moe_expert_bytes(int32_t hidden, int32_t ffn, int32_t quant) {
+    if (hidden <= 0 || ffn <= 0 || hidden % 32 || ffn % 32 || (quant != MOE_Q4B32 && quant != MOE_Q2B32)) return -1;
+    return 3LL * hidden * ffn / 32 * (quant == MOE_Q4B32 ? 18 : 10);
+}
+
+moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
+    if (!out) return fail(MOE_EINVAL, "out is NULL");
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    moe_ctx* c = new (std::nothrow) moe_ctx;
+    if (!c) return fail(MOE_ENOMEM, "host allocation failed");
+    c->cfg = *cfg;
+    c->g = make_geom(cfg->hidden, cfg->ffn, cfg->n_experts, cfg->n_shared, cfg->top_k, cfg->quant, cfg->n_layers);
+    const Geom& g = c->g;
+    hipError_t e = hipSetDevice(cfg->device);
+    if (e != hipSuccess) { free_ctx(c); return fail(MOE_EHIP, "hipSetDevice: %s", hipGetErrorString(e)); }
+    const int L = cfg->n_layers, ES = cfg->n_experts + cfg->n_shared;
+    c->arena_bytes = (uint64_t)L * ES * g.slot_bytes;
+    size_t free_b = 0, total_b = 0;
+    hipMemGetInfo(&free_b, &total_b);
+    if (c->arena_bytes + (64ull << 20) > free_b) {
+        free_ctx(c);
+        return fail(MOE_ENOMEM, "expert arena of %llu bytes does not fit in %llu free bytes",
+                    (unsigned long long)((uint64_t)L * ES * g.slot_bytes), (unsigned long long)free_b);
+    }
+    if (hipMalloc(&c->arena, c->arena_bytes) != hipSuccess) {
+        hipGetLastError();
+        free_ctx(c);
+        return fail(MOE_ENOMEM, "hipMalloc of the %llu-byte expert arena failed", (unsigned long long)c->arena_bytes);
+    }
+    if (hipMalloc(&c->routers, (size_t)L * g.E * g.H * 2) != hipSuccess ||
+        hipMalloc(&c->biases, (size_t)L * g.E * 4) != hipSuccess) {
+        hipGetLastError();
+        free_ctx(c);
+        return fail(MOE_ENOMEM, "router allocation failed");
+    }
+    // scratch for the decode path (T <= 8)
+    const int Td = std::min(cfg->max_tokens, kMaxDecodeT);
+    c->decode_T = Td;
+    c->maxA = std::min(g.E, kMaxDecodeT * g.k) + g.S;
+    const int nbHp = g.gu.nch * 4, nbFp = g.dn.nch * 4;
+    Carver cv;
+    const size_t o_logits = cv.take<double>((size_t)kMaxDecodeT * g.E);
+    const size_t o_sx = cv.take<float>((size_t)nbHp * 16);
+    const size_t o_ids = cv.take<int32_t>((size_t)kMaxDecodeT * g.k);
+    const size_t o_w = cv.take<float>((size_t)kMaxDecodeT * g.k);
+    const size_t o_off = cv.take<int32_t>((size_t)g.E + 1);
+    const size_t o_perm = cv.take<int32_t>((size_t)kMaxDecodeT * g.k);
+    const size_t o_inv = cv.take<int32_t>((size_t)kMaxDecodeT * g.k);
+    const size_t o_nact = cv.take<int32_t>(1);
+    const size_t o_act = cv.take<int32_t>((size_t)c->maxA);
+    const size_t o_wtab = cv.take<float>((size_t)c->maxA * kMaxDecodeT);
+    const size_t o_afrag = cv.take<uint32_t>((size_t)c->maxA * nbFp * 64 * 4);
+    const size_t o_spart = cv.take<float>((size_t)c->maxA * nbFp * 32);
+    const size_t o_x0 = cv.take<uint16_t>((size_t)kMaxDecodeT * g.H);
+    const size_t o_x1 = cv.take<uint16_t>((size_t)kMaxDecodeT * g.H);
+    c->scratch_bytes = cv.off;
+    if (hipMalloc(&c->scratch, c->scratch_bytes) != hipSuccess) {
+        hipGetLastError();
+        free_ctx(c);
+        return fail(MOE_ENOMEM, "scratch allocation failed");
+    }
+    uint8_t* b = c->scratch;
+    c->rb.logits = (double*)(b + o_logits);
+    c->rb.sx = (float*)(b + o_sx);
+    c->rb.ids = (int32_t*)(b + o_ids);
+    c->rb.w = (float*)(b + o_w);
+    c->rb.offsets = (int32_t*)(b + o_off);
+    c->rb.perm = (int32_t*)(b + o_perm);
+    c->rb.inv = (int32_t*)(b + o_inv);
+    c->rb.nact = (int32_t*)(b + o_nact);
+    c->rb.act = (int32_t*)(b + o_act);
+    c->rb.wtab = (float*)(b + o_wtab);
+    c->db.afrag = (uint32_t*)(b + o_afrag);
+    c->db.spart = (float*)(b + o_spart);
+    c->xbuf[0] = (uint16_t*)(b + o_x0);
+    c->xbuf[1] = (uint16_t*)(b + o_x1);
+    if (hipMemset(c->scratch, 0, c->scratch_bytes) != hipSuccess ||
+        hipMemset(c->biases, 0, (size_t)L * g.E * 4) != hipSuccess) {
+        free_ctx(c);
+        return fail(MOE_EHIP, "scratch initialisation failed");
+    }
+    // bounded staging for uploads
+    if (hipStreamCreateWithFlags(&c->load_stream, hipStreamNonBlocking) != hipSuccess) {
+        free_ctx(c);
+        return fail(MOE_EHIP, "stream creation failed");
+    }
+    for (int i = 0; i < 2; ++i) {
+        if (hipHostMalloc(&c->host_stage[i], kStagingBytes, hipHostMallocDefault) != hipSuccess ||
+            hipMalloc(&c->dev_stage[i], kStagingBytes) != hipSuccess ||
+            hipEventCreateWithFlags(&c->stage_done[i], hipEventDisableTiming) != hipSuccess) {
+            hipGetLastError();
+            free_ctx(c);
+            return fail(MOE_ENOMEM, "staging allocation failed");
+        }
+    }
+    c->router_loaded.assign(L, 0);
+    c->expert_loaded.assign((size_t)L * ES, 0);
+    *out = c;
+    return MOE_OK;
+}
+
+moe_status moe_memory_bytes(const moe_ctx* c, uint64_t* arena_bytes, uint64_t* scratch_bytes) {
+    if (!c) return fail(MOE_EINVAL, "ctx is NULL");
+    if (arena_bytes) *arena_bytes = c->arena_bytes;
+    if (scratch_bytes) *scratch_bytes = c->scratch_bytes;
+    return MOE_OK;
+}
+
+moe_status moe_load_experts(moe_ctx* c, const moe_layer_weights* w) {
+    if (!c || !w) return fail(MOE_EINVAL, "ctx or weights is NULL");
+    if (c->poisoned) return fail(MOE_ESTATE, "context is poisoned by an earlier HIP failure");
+    const Geom& g = c->g;
+    const int ES = g.E + g.S;
+    if (w->layer < 0 || w->layer >= g.L) return fail(MOE_EINVAL, "layer %d outside [0, %d)", w->layer, g.L);
+    if (w->expert_count < 0 || w->expert_begin < 0 || w->expert_begin + w->expert_count > ES)
+        return fail(MOE_EINVAL, "experts [%d, %d) outside [0, %d)", w->expert_begin, w->expert_begin + w->expert_count, ES);
+    if (w->expert_count > 0 && !w->experts) return fail(MOE_EINVAL, "experts is NULL");
+    if ((uint64_t)w->experts_bytes != (uint64_t)w->expert_count * (uint64_t)g.canon_expert_bytes)
+        return fail(MOE_EINVAL, "experts_bytes %zu != %d experts x %lld bytes", w->experts_bytes, w->expert_count,
+                    (long long)g.canon_expert_bytes);
+    if (!w->router_w && w->router_bias) return fail(MOE_EINVAL, "router_bias without router_w");
+    HIP_TRY(c, hipSetDevice(c->cfg.device));
+    if (w->router_w) {
+        HIP_TRY(c, hipMemcpy(c->routers + (size_t)w->layer * g.E * g.H, w->router_w, (size_t)g.E * g.H * 2,
+                             hipMemcpyHostToDevice));
+        float* bdst = c->biases + (size_t)w->layer * g.E;
+        if (w->router_bias)
+            HIP_TRY(c, hipMemcpy(bdst, w->router_bias, (size_t)g.E * 4, hipMemcpyHostToDevice));
+        else
+            HIP_TRY(c, hipMemset(bdst, 0, (size_t)g.E * 4));
+        c->router_loaded[w->layer] = 1;
+    }
+    if (w->expert_count > 0) {
+        const int per = (int)std::max<int64_t>(1, (int64_t)kStagingBytes / g.canon_expert_bytes);
+        if ((size_t)g.canon_expert_bytes > kStagingBytes)
+            return fail(MOE_EINVAL, "one expert (%lld bytes) exceeds the staging buffer", (long long)g.canon_expert_bytes);
+        uint8_t* layer_slots = c->arena + ((size_t)w->layer * ES) * g.slot_bytes;
+        int buf = 0;
+        for (int e0 = 0; e0 < w->expert_count; e0 += per, buf ^= 1) {
+            const int n = std::min(per, w->expert_count - e0);
+            const size_t bytes = (size_t)n * g.canon_expert_bytes;
+            HIP_TRY(c, hipEventSynchronize(c->stage_done[buf]));  // host staging buffer free again
+            memcpy(c->host_stage[buf], w->experts + (size_t)e0 * g.canon_expert_bytes, bytes);
+            HIP_TRY(c, hipMemcpyAsync(c->dev_stage[buf], c->host_stage[buf], bytes, hipMemcpyHostToDevice,
+                                      c->load_stream));
+            HIP_TRY(c, hipEventRecord(c->stage_done[buf], c->load_stream));
+            HIP_TRY(c, launch_repack(c->dev_stage[buf], layer_slots + (size_t)(w->expert_begin + e0) * g.slot_bytes, n,
+                                     g, c->load_stream));
+        }
+        HIP_TRY(c, hipStreamSynchronize(c->load_stream));
+        for (int i = 0; i < w->expert_count; ++i) c->expert_loaded[(size_t)w->layer * ES + w->expert_begin + i] = 1;
+    }
+    return MOE_OK;
+}
+
+namespace {
+
+moe_status check_layer_ready(moe_ctx* c, int layer, bool need_experts) {
+    if (!c->router_loaded[layer]) return fail(MOE_ESTATE, "router of layer %d is not loaded", layer);
+    if (need_experts) {
+        const int ES = c->g.E + c->g.S;
+        for (int e = 0; e < ES; ++e)
+            if (!c->expert_loaded[(size_t)layer * ES + e])
+                return fail(MOE_ESTATE, "expert %d of layer %d is not loaded", e, layer);
+    }
+    return MOE_OK;
+}
+
+moe_status route_decode(moe_ctx* c, int layer, const uint16_t* x, int T, int32_t* trace_ids, float* trace_w,
+                        hipStream_t st) {
+    const Geom& g = c->g;
+    HIP_TRY(c, launch_router_decode(x, T, c->routers + (size_t)layer * g.E * g.H, c->biases + (size_t)layer * g.E, g,
+                                    c->rb, st));
+    HIP_TRY(c, launch_topk_sort_decode(T, g, c->rb, trace_ids, trace_w, st));
+    return MOE_OK;
+}
+
+}  // namespace
+
+moe_status moe_route(moe_ctx* c, int32_t layer, const void* x, int32_t T, int32_t* ids, float* w, int32_t* offsets,
+                     int32_t* perm, void* hip_stream) {
+    if (!c) return fail(MOE_EINVAL, "ctx is NULL");
+    if (c->poisoned) return fail(MOE_ESTATE, "context is poisoned by an earlier HIP failure");
+    const Geom& g = c->g;
+    if (layer < 0 || layer >= g.L) return fail(MOE_EINVAL, "layer %d outside [0, %d)", layer, g.L);
+    if (T < 0) return fail(MOE_EINVAL, "T %d is negative", T);
+    if (T > c->cfg.max_tokens) return fail(MOE_ERANGE, "T %d above max_tokens %d", T, c->cfg.max_tokens);
+    if (T == 0) return MOE_OK;
+    if (!x || !ids || !w) return fail(MOE_EINVAL, "x, ids and w are required");
+    if (!aligned16(x)) return fail(MOE_EINVAL, "x must be 16-byte aligned");
+    moe_status s = check_layer_ready(c, layer, false);
+    if (s != MOE_OK) return s;
+    if (T > kMaxDecodeT) return fail(MOE_EINVAL, "T %d: only windows of at most %d tokens are supported", T, kMaxDecodeT);
+    hipStream_t st = (hipStream_t)hip_stream;
+    HIP_TRY(c, hipSetDevice(c->cfg.device));
+    s = route_decode(c, layer, (const uint16_t*)x, T, nullptr, nullptr, st);
+    if (s != MOE_OK) return s;
+    const size_t P = (size_t)T * g.k;
+    HIP_TRY(c, hipMemcpyAsync(ids, c->rb.ids, P * 4, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(c, hipMemcpyAsync(w, c->rb.w, P * 4, hipMemcpyDeviceToDevice, st));
+    if (offsets) HIP_TRY(c, hipMemcpyAsync(offsets, c->rb.offsets, ((size_t)g.E + 1) * 4, hipMemcpyDeviceToDevice, st));
+    if (perm) HIP_TRY(c, hipMemcpyAsync(perm, c->rb.perm, P * 4, hipMemcpyDeviceToDevice, st));
+    return MOE_OK;
+}
+
+moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
+    if (!c || !a) return fail(MOE_EINVAL, "ctx or args is NULL");
+    if (c->poisoned) return fail(MOE_ESTATE, "context is poisoned by an earlier HIP failure");
+    const Geom& g = c->g;
+    if (a->layer_count < 1 || a->layer_begin < 0 || a->layer_begin + a->layer_count > g.L)
+        return fail(MOE_EINVAL, "layers [%d, %d) outside [0, %d)", a->layer_begin, a->layer_begin + a->layer_count, g.L);
+    if (a->T < 0) return fail(MOE_EINVAL, "T %d is negative", a->T);
+    if (a->T > c->cfg.max_tokens) return fail(MOE_ERANGE, "T %d above max_tokens %d", a->T, c->cfg.max_tokens);
+    if (a->flags & ~MOE_FWD_RESIDUAL) return fail(MOE_EINVAL, "unknown flags 0x%x", a->flags);
+    if (a->T == 0) return MOE_OK;
+    if (!a->x || !a->y) return fail(MOE_EINVAL, "x and y are required");
+    if (!aligned16(a->x) || !aligned16(a->y) || (a->trace_x && !aligned16(a->trace_x)))
+        return fail(MOE_EINVAL, "x, y and trace_x must be 16-byte aligned");
+    if (a->x == a->y) return fail(MOE_EINVAL, "y may not alias x");
+    for (int l = a->layer_begin; l < a->layer_begin + a->layer_count; ++l) {
+        moe_status s = check_layer_ready(c, l, true);
+        if (s != MOE_OK) return s;
+    }
+    const int T = a->T;
+    if (T > kMaxDecodeT) return fail(MOE_EINVAL, "T %d: only windows of at most %d tokens are supported", T, kMaxDecodeT);
+    hipStream_t st = (hipStream_t)hip_stream;
+    HIP_TRY(c, hipSetDevice(c->cfg.device));
+    const int ES = g.E + g.S;
+    const size_t xbytes = (size_t)T * g.H * 2;
+    const uint16_t* xin = (const uint16_t*)a->x;
+    for (int i = 0; i < a->layer_count; ++i) {
+        const int l = a->layer_begin + i;
+        const bool last = i == a->layer_count - 1;
+        uint16_t* yout = last ? (uint16_t*)a->y : c->xbuf[i & 1];
+        if (a->trace_x)
+            HIP_TRY(c, hipMemcpyAsync((uint8_t*)a->trace_x + (size_t)i * xbytes, xin, xbytes, hipMemcpyDeviceToDevice, st));
+        moe_status s = route_decode(c, l, xin, T, a->trace_ids ? a->trace_ids + (size_t)i * T * g.k : nullptr,
+                                    a->trace_w ? a->trace_w + (size_t)i * T * g.k : nullptr, st);
+        if (s != MOE_OK) return s;
+        const uint8_t* slots = c->arena + (size_t)l * ES * g.slot_bytes;
+        HIP_TRY(c, launch_gateup_decode(xin, T, slots, g, c->rb, c->db, st));
+        HIP_TRY(c, launch_down_decode(xin, T, slots, g, c->rb, c->db, yout, a->flags & MOE_FWD_RESIDUAL, st));
+        xin = yout;
+    }
+    return MOE_OK;
+}
+
+moe_status moe_destroy(moe_ctx* c) {
+    if (!c) return MOE_OK;
+    hipSetDevice(c->cfg.device);
+    hipDeviceSynchronize();
+    free_ctx(c);
+    return MOE_OK;
+}
+
+}  // extern "C"

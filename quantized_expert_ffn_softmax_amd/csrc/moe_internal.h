@@ -1,0 +1,116 @@
+// Internal declarations shared by the host runtime and the kernels of libmoe.
+//
+// Device layout of one expert slot (gfx950 decode/prefill format)
+// ----------------------------------------------------------------
+// A quantised matrix [R x K] (R output rows, K input dim, blocks of 32 along K)
+// is stored as R/16 "row tiles" of 16 rows.  A row tile is a sequence of
+// chunks of 4 blocks (K padded up to a multiple of 128 with zero-scale
+// blocks).  One chunk is laid out for a 64-lane wave that feeds the bf16
+// MFMA v_mfma_f32_16x16x32_bf16 with the weights as its B operand:
+//
+//   codes : 64 lanes x CW bytes, lane l = n + 16*g holds row n (0..15) of the
+//           tile and k-slice g (elements 8g..8g+7 of each block)
+//           q4 (CW = 16): word j = block j of the chunk; nibble p (bits 4p)
+//                          holds element 8g+2p, nibble p+4 (bits 16+4p) holds
+//                          element 8g+2p+1, p = 0..3
+//           q2 (CW = 8):  word j = blocks 2j (bits 0..7, 16..23) and 2j+1
+//                          (bits 8..15, 24..31); inside a block half, bits 2p
+//                          hold element 8g+2p and bits 16+2p element 8g+2p+1
+//   scales: 16 rows x 4 fp16, row n's scales of blocks 0..3 (8 bytes)
+//
+// With that bit order, (word >> s) & mask | 0x4300 0x4300 is the bf16 pair
+// (128 + q_k, 128 + q_k+1) for consecutive k, so a code is turned into an
+// exact MFMA operand with one shift and one and-or; the offset 128 + o is
+// removed after the contraction with the per-block sums of the other operand.
+//
+// An expert slot holds G (F/16 row tiles, K = H), then U (same), then D
+// (H/16 row tiles, K = F), and is padded to a multiple of 256 bytes.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kChunkBlocks = 4;
+constexpr int kMaxDecodeT = 8;   // decode path: tokens share one 16-row MFMA tile (hi/lo halves)
+constexpr int kMaxTopK = 16;
+constexpr int kMaxExperts = 1024;
+
+struct MatGeom {
+    int rows;        // R
+    int K;           // input dim
+    int nb;          // K / 32
+    int nch;         // chunks per row tile (nb padded to a multiple of 4, / 4)
+    int chunk_bytes; // q4: 1152, q2: 640
+    int64_t tile_bytes;
+    int64_t bytes;   // rows/16 * tile_bytes
+};
+
+struct Geom {
+    int H, F, E, S, k, fmt, L;
+    MatGeom gu;      // G and U: [F x H]
+    MatGeom dn;      // D: [H x F]
+    int64_t g_off, u_off, d_off;
+    int64_t slot_bytes;
+    int64_t canon_expert_bytes;
+};
+
+inline int code_bytes_per_lane(int fmt) { return fmt == 1 ? 16 : 8; }
+
+inline MatGeom make_mat(int rows, int K, int fmt) {
+    MatGeom m;
+    m.rows = rows;
+    m.K = K;
+    m.nb = K / 32;
+    m.nch = (m.nb + kChunkBlocks - 1) / kChunkBlocks;
+    m.chunk_bytes = 64 * code_bytes_per_lane(fmt) + 16 * kChunkBlocks * 2;
+    m.tile_bytes = (int64_t)m.nch * m.chunk_bytes;
+    m.bytes = (int64_t)(rows / 16) * m.tile_bytes;
+    return m;
+}
+
+inline Geom make_geom(int H, int F, int E, int S, int k, int fmt, int L) {
+    Geom g;
+    g.H = H; g.F = F; g.E = E; g.S = S; g.k = k; g.fmt = fmt; g.L = L;
+    g.gu = make_mat(F, H, fmt);
+    g.dn = make_mat(H, F, fmt);
+    g.g_off = 0;
+    g.u_off = g.gu.bytes;
+    g.d_off = 2 * g.gu.bytes;
+    g.slot_bytes = (2 * g.gu.bytes + g.dn.bytes + 255) / 256 * 256;
+    g.canon_expert_bytes = 3LL * H * F / 32 * (fmt == 1 ? 18 : 10);
+    return g;
+}
+
+// Per-call routing scratch (device), sized for max_tokens by the runtime.
+struct RouteBufs {
+    double* logits;   // [T x E]
+    float* sx;        // [nbH x 16] per-block sums of x rows (decode path)
+    int32_t* ids;     // [T x k]
+    float* w;         // [T x k]
+    int32_t* offsets; // [E + 1]
+    int32_t* perm;    // [T*k]
+    int32_t* inv;     // [T*k]
+    int32_t* nact;    // [1]   number of active experts incl. the shared one
+    int32_t* act;     // [maxA] expert id of active slot a (ascending; shared last)
+    float* wtab;      // [maxA x 8] routing weight of token t for active slot a (decode)
+};
+
+// Decode FFN scratch.
+struct DecodeBufs {
+    uint32_t* afrag;  // [maxA x nbF_pad x 64 x 4] bf16 pairs, down-projection A operand
+    float* spart;     // [maxA x nbF_pad x 2 x 16] per-half-block sums of afrag rows
+};
+
+// Launchers (return hipGetLastError()).
+hipError_t launch_repack(const uint8_t* canon, uint8_t* slots, int count, const Geom& g, hipStream_t st);
+hipError_t launch_router_decode(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const Geom& g,
+                                RouteBufs rb, hipStream_t st);
+hipError_t launch_topk_sort_decode(int T, const Geom& g, RouteBufs rb, int32_t* trace_ids, float* trace_w,
+                                   hipStream_t st);
+hipError_t launch_gateup_decode(const uint16_t* x, int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb,
+                                DecodeBufs db, hipStream_t st);
+hipError_t launch_down_decode(const uint16_t* x, int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb,
+                              DecodeBufs db, uint16_t* y, int residual, hipStream_t st);
+
+}  // namespace moe
