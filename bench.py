@@ -1,0 +1,262 @@
+"""Benchmark of the MI355X sparse-MoE layer (one GPU).
+
+Default workload (the headline metric): one Qwen3.8-Flash-Next-shaped MoE
+layer decoding a 4-token verify window -- hidden 2560, 512 experts, top-10,
+expert FF 640, q2b32 experts, Zipf(1.1) router bias.  A step is one
+moe_forward call through the whole hot path (router, top-k, weights, counting
+sort, dequant + gate/up + SwiGLU, down + weighted combine) on one layer and
+one window of 4 tokens.  Steps cycle over 48 resident layers of that shape
+(every layer has its own router, Zipf permutation and 512 experts) and 16
+distinct input windows, so that successive steps read different expert
+weights and the 256 MB Infinity Cache does not serve repeated reads.
+
+Other workloads (--workload): C3 (the 48-layer chain with residual adds at
+window 1/4/8) and C4 (the 43-layer DeepSeek-shaped chain, 256+1 experts,
+q4b32); a step is then one full chain pass.
+
+Printed: one JSON line with tokens/s, HBM GB/s on expert bytes, the roofline
+of the dominant kernel (gate/up, measured with HIP events recorded around
+each launch on the launch stream) and the fp64 oracle's throughput on the
+host cores as a CPU baseline.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s on expert weights (decode, window 4)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=960)
+    p.add_argument("--warmup", type=int, default=96)
+    p.add_argument("--workload", default="C2", choices=["C2", "C3", "C4"])
+    p.add_argument("--T", type=int, default=4, help="tokens per window")
+    p.add_argument("--layers", type=int, default=0, help="resident layers (default: 48 for C2/C3, 43 for C4)")
+    p.add_argument("--windows", type=int, default=16)
+    p.add_argument("--seed", type=int, default=1)
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU-baseline leg")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported (no collectives)"}))
+        sys.exit(2)
+    import torch
+
+    import moe_inputs as mi
+    from moe_inputs.configs import C2, C3, C4
+    from quantized_expert_ffn_softmax_amd import MoEContext
+
+    cfg = {"C2": C2, "C3": C3, "C4": C4}[args.workload]
+    L = args.layers or (43 if args.workload == "C4" else 48)
+    T = args.T
+    chain = args.workload in ("C3", "C4")
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+
+    log(f"[bench] workload {args.workload}: H={cfg.H} F={cfg.F} E={cfg.E}+{cfg.S} k={cfg.k} layers={L} T={T}")
+    t0 = time.time()
+    ctx = MoEContext(cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, L, cfg.fmt, 8)
+    for layer in range(L):
+        W, b, ex = mi.layer_inputs(cfg, args.seed, layer)
+        ctx.load(layer, router_w=W, router_bias=b, experts=ex)
+        del ex
+        if layer % 8 == 7 or layer == L - 1:
+            log(f"[bench] loaded {layer + 1}/{L} layers ({time.time() - t0:.0f}s)")
+    xs = [torch.from_numpy(mi.gen_x(args.seed, w, T, cfg.H).view(np.int16)).view(torch.bfloat16).to(dev)
+          for w in range(args.windows)]
+    y = torch.empty_like(xs[0])
+
+    def step(i, profile=False, trace_ids=None):
+        if chain:
+            return ctx.forward(xs[i % len(xs)], 0, L, residual=True, y=y, profile=profile)
+        layer = i % L
+        from quantized_expert_ffn_softmax_amd import moe_forward, MOE_FWD_PROFILE
+        moe_forward(ctx.handle, xs[i % len(xs)], y, T, layer, 1, MOE_FWD_PROFILE if profile else 0,
+                    None, trace_ids, None)
+
+    # ---- warmup + timed region (no profiling events)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    tokens_per_s = T * args.steps / (ms_total / 1e3)
+    log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us)")
+
+    # ---- routing of every (layer, window) pair used: distinct experts -> algorithmic bytes
+    n_pairs = L if chain else int(np.lcm(L, len(xs)))
+    n_steps_acct = len(xs) if chain else n_pairs
+    U = {}
+    for i in range(n_steps_acct):
+        if chain:
+            _, _, tid, _ = ctx.forward(xs[i % len(xs)], 0, L, residual=True, trace=True)
+            for layer in range(L):
+                U[(layer, i % len(xs))] = len(np.unique(tid[layer].cpu().numpy()))
+        else:
+            layer = i % L
+            ids, _, _, _ = ctx.route(layer, xs[i % len(xs)])
+            U[(layer, i % len(xs))] = len(np.unique(ids.cpu().numpy()))
+    expert_bytes = cfg.expert_bytes
+    gu_bytes = 2 * expert_bytes // 3  # G and U of one expert
+    dn_bytes = expert_bytes // 3
+
+    def step_bytes(i):
+        w = i % len(xs)
+        if chain:
+            return sum((U[(l, w)] + cfg.S) * expert_bytes + cfg.router_bytes for l in range(L))
+        layer = i % L
+        return (U[(layer, w)] + cfg.S) * expert_bytes + cfg.router_bytes
+
+    total_bytes = sum(step_bytes(i) for i in range(args.steps))
+    hbm_gbps = total_bytes / (ms_total / 1e3) / 1e9
+
+    # ---- profiled pass: HIP events around every kernel, on the launch stream
+    nprof = min(args.steps, 4 * n_pairs if not chain else len(xs))
+    ctx.profile_read()
+    for i in range(nprof):
+        step(i, profile=True)
+    torch.cuda.synchronize()
+    recs = ctx.profile_read()
+    per_kernel = {}
+    for name, layer, ms in recs:
+        per_kernel.setdefault(name, []).append(ms)
+    # algorithmic bytes of the gate/up launches of the profiled steps, in launch order
+    gu_launch_bytes, dn_launch_bytes = [], []
+    for i in range(nprof):
+        w = i % len(xs)
+        layers = range(L) if chain else [i % L]
+        for layer in layers:
+            gu_launch_bytes.append((U[(layer, w)] + cfg.S) * gu_bytes)
+            dn_launch_bytes.append((U[(layer, w)] + cfg.S) * dn_bytes)
+    gu_ms = per_kernel.get("gateup", [])
+    dn_ms = per_kernel.get("down", [])
+    assert len(gu_ms) == len(gu_launch_bytes), (len(gu_ms), len(gu_launch_bytes))
+    gu_avg_us = 1e3 * float(np.mean(gu_ms))
+    gu_achieved = float(np.sum(gu_launch_bytes)) / (float(np.sum(gu_ms)) / 1e3) / 1e9
+    dn_achieved = float(np.sum(dn_launch_bytes)) / (float(np.sum(dn_ms)) / 1e3) / 1e9
+    kernels_us = {k: round(1e3 * float(np.mean(v)), 2) for k, v in per_kernel.items()}
+    log(f"[bench] per-kernel mean us (events): {kernels_us}")
+    log(f"[bench] gate/up {gu_achieved:.0f} GB/s, down {dn_achieved:.0f} GB/s, layer {hbm_gbps:.0f} GB/s")
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "gateup_traffic.json")
+    if os.path.exists(tpath) and not chain:
+        with open(tpath) as f:
+            tr = json.load(f)
+        if tr.get("workload") == args.workload and tr.get("kernel_sha") == kernel_sha():
+            traffic = tr.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{args.workload}: " + ("one Qwen-shaped MoE decode layer per step, cycling "
+                                                  f"{L} resident layers and {len(xs)} windows" if not chain else
+                                                  f"{L}-layer MoE-only decode chain with residual per step")),
+            "T": T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "S": cfg.S, "k": cfg.k, "layers_resident": L,
+            "quant": "q4b32" if cfg.fmt == 1 else "q2b32", "seed": args.seed,
+        },
+        "hbm_GBps": round(hbm_gbps, 1),
+        "hbm_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+        "kernels_us": kernels_us,
+        "roofline": {
+            "kernel": "k_gateup_decode",
+            "bound": "hbm",
+            "achieved": round(gu_achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(gu_achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(gu_avg_us, 3),
+            "bytes_per_launch": round(float(np.mean(gu_launch_bytes)), 1),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, args, L, chain, T)
+    ctx.close()
+    print(json.dumps(result), flush=True)
+
+
+def kernel_sha():
+    import hashlib
+    with open(os.path.join(ROOT, "quantized_expert_ffn_softmax_amd", "csrc", "moe_kernels.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def cpu_baseline(cfg, args, L, chain, T):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    import moe_inputs as mi
+    import oracle
+    threads = oracle.num_threads()
+    t_start = time.perf_counter()
+    n_tokens = 0
+    calls = 0
+    if not chain:
+        W, b, ex = mi.layer_inputs(cfg, args.seed, 0)
+        t_start = time.perf_counter()
+        while time.perf_counter() - t_start < args.cpu_seconds and calls < 256:
+            x = mi.gen_x(args.seed, calls % args.windows, T, cfg.H)
+            oracle.moe_layer(x, cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, cfg.fmt, W, b, ex, cfg.expert_bytes)
+            n_tokens += T
+            calls += 1
+        dt = time.perf_counter() - t_start
+        sample = f"{calls} calls of layer 0 on {T}-token windows (input generation excluded)"
+    else:
+        # a chain step needs every layer; time the layers one by one and extrapolate nothing:
+        # the sample is the first layers of one chain step
+        x = mi.gen_x(args.seed, 0, T, cfg.H)
+        t_layers = 0.0
+        for layer in range(L):
+            W, b, ex = mi.layer_inputs(cfg, args.seed, layer)
+            t1 = time.perf_counter()
+            y, *_ = oracle.moe_layer(x, cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, cfg.fmt, W, b, ex, cfg.expert_bytes)
+            x = oracle.residual_bf16(x, y)
+            t_layers += time.perf_counter() - t1
+            calls += 1
+            if t_layers > args.cpu_seconds:
+                break
+        dt = t_layers
+        n_tokens = T * calls / L  # fraction of one chain step
+        sample = f"first {calls} of {L} layers of one chain step, T={T} (input generation excluded)"
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -75,7 +75,7 @@ typedef enum { MOE_Q4B32 = 1, MOE_Q2B32 = 2 } moe_quant;
 
 /* Layer geometry, fixed for the lifetime of a context (E and k are runtime
  * values, as the pages' engine reads them from the model file).
- *   hidden, ffn : H and F, positive multiples of 32
+ *   hidden, ffn : H and F, positive multiples of 32, H <= 4096, F <= 2048
  *   n_experts   : E routed experts, 1..1024
  *   n_shared    : 0 or 1 always-on shared expert (expert index E)
  *   top_k       : k in [1, min(E, 16)]
@@ -105,6 +105,7 @@ typedef struct {
 } moe_layer_weights;
 
 #define MOE_FWD_RESIDUAL 1 /* x_{l+1} = bf16(fp32(x_l) + y_l); else x_{l+1} = bf16(y_l) */
+#define MOE_FWD_PROFILE 2  /* record a HIP event pair around every kernel (read with moe_profile_read) */
 
 /* One forward pass through layers [layer_begin, layer_begin + layer_count).
  *   x      : [T x H] bf16, device, input of the first layer
@@ -158,6 +159,33 @@ moe_status moe_destroy(moe_ctx* ctx);
 
 /* Thread-local text of the last non-OK status returned to this thread. */
 const char* moe_last_error(void);
+
+/* Kernel kinds reported by moe_profile_read. */
+typedef enum {
+    MOE_K_ROUTER = 0,       /* router GEMV, decode path */
+    MOE_K_TOPK_SORT = 1,    /* top-k, weights, counting sort, decode path */
+    MOE_K_GATEUP = 2,       /* dequant + gate/up GEMV + SwiGLU, decode path */
+    MOE_K_DOWN = 3,         /* dequant + down GEMV per expert, decode path */
+    MOE_K_COMBINE = 4,      /* ordered weighted combine (+ residual), decode path */
+    MOE_K_PF_ROUTER = 5,    /* prefill router */
+    MOE_K_PF_TOPK = 6,      /* prefill top-k + weights */
+    MOE_K_PF_SORT = 7,      /* prefill counting sort */
+    MOE_K_PF_GEMM1 = 8,     /* prefill grouped GEMM gate/up + SwiGLU */
+    MOE_K_PF_GEMM2 = 9,     /* prefill grouped GEMM down */
+    MOE_K_PF_COMBINE = 10   /* prefill weighted combine */
+} moe_kernel_kind;
+
+typedef struct {
+    int32_t kernel; /* moe_kernel_kind */
+    int32_t layer;
+    float ms;       /* hipEventElapsedTime between the events around the launch */
+} moe_kernel_time;
+
+/* Durations of the kernels launched by moe_forward calls made with
+ * MOE_FWD_PROFILE since the previous read, in launch order.  Waits for those
+ * events, writes at most cap records, sets *n_out to the number written and
+ * forgets all recorded launches.  Profiling keeps at most 65536 launches. */
+moe_status moe_profile_read(moe_ctx* ctx, moe_kernel_time* out, int32_t cap, int32_t* n_out);
 
 /* Canonical bytes of one expert (3*H*F/32 blocks), or -1 for a bad shape. */
 int64_t moe_expert_bytes(int32_t hidden, int32_t ffn, int32_t quant);

@@ -62,8 +62,15 @@ def lib():
         L.oracle_moe_layer.restype = None
         L.oracle_residual_bf16.argtypes = [ctypes.c_uint16, f64]
         L.oracle_residual_bf16.restype = ctypes.c_uint16
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = i32
         _lib = L
     return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads used by the oracle's parallel loops."""
+    return int(lib().oracle_num_threads())
 
 
 def _p(a):

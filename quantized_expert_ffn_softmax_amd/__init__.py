@@ -20,12 +20,15 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_ESTATE, MOE_ERANGE = 0, -1, -2, -3, -4, -5
 MOE_Q4B32, MOE_Q2B32 = 1, 2
 MOE_FWD_RESIDUAL = 1
+MOE_FWD_PROFILE = 2
+KERNEL_NAMES = {0: "router", 1: "topk_sort", 2: "gateup", 3: "down", 4: "combine", 5: "pf_router", 6: "pf_topk",
+                7: "pf_sort", 8: "pf_gemm1", 9: "pf_gemm2", 10: "pf_combine"}
 MOE_ABI_VERSION = 1
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOMEM", -3: "MOE_EHIP", -4: "MOE_ESTATE", -5: "MOE_ERANGE"}
 
 # Every symbol include/moe.h declares.
 EXPORTED = ("moe_create", "moe_load_experts", "moe_route", "moe_forward", "moe_destroy", "moe_last_error",
-            "moe_expert_bytes", "moe_memory_bytes")
+            "moe_expert_bytes", "moe_memory_bytes", "moe_profile_read")
 
 
 class moe_config(ctypes.Structure):
@@ -43,6 +46,10 @@ class moe_fwd_args(ctypes.Structure):
     _fields_ = [("layer_begin", ctypes.c_int32), ("layer_count", ctypes.c_int32), ("T", ctypes.c_int32),
                 ("flags", ctypes.c_int32), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("trace_x", ctypes.c_void_p), ("trace_ids", ctypes.c_void_p), ("trace_w", ctypes.c_void_p)]
+
+
+class moe_kernel_time(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("layer", ctypes.c_int32), ("ms", ctypes.c_float)]
 
 
 class MoEError(RuntimeError):
@@ -72,7 +79,9 @@ def lib():
         L.moe_expert_bytes.argtypes = [i32, i32, i32]
         L.moe_expert_bytes.restype = ctypes.c_int64
         L.moe_memory_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)]
-        for f in ("moe_create", "moe_load_experts", "moe_route", "moe_forward", "moe_destroy", "moe_memory_bytes"):
+        L.moe_profile_read.argtypes = [vp, ctypes.POINTER(moe_kernel_time), i32, ctypes.POINTER(i32)]
+        for f in ("moe_create", "moe_load_experts", "moe_route", "moe_forward", "moe_destroy", "moe_memory_bytes",
+                  "moe_profile_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -147,6 +156,14 @@ def moe_memory_bytes(ctx):
     return a.value, s.value
 
 
+def moe_profile_read(ctx, cap=65536):
+    """[(kernel_name, layer, ms), ...] of the profiled launches since the last read."""
+    buf = (moe_kernel_time * cap)()
+    n = ctypes.c_int32()
+    _check(lib().moe_profile_read(ctx, buf, cap, ctypes.byref(n)))
+    return [(KERNEL_NAMES.get(buf[i].kernel, buf[i].kernel), buf[i].layer, buf[i].ms) for i in range(n.value)]
+
+
 # --------------------------------------------------------------- convenience
 class MoEContext:
     """Owns one moe_ctx; tensors are torch CUDA tensors, weights numpy arrays."""
@@ -179,7 +196,8 @@ class MoEContext:
         moe_route(self.handle, layer, x, T, ids, w, offsets, perm, stream)
         return ids, w, offsets, perm
 
-    def forward(self, x, layer_begin=0, layer_count=1, residual=False, trace=False, y=None, stream=None):
+    def forward(self, x, layer_begin=0, layer_count=1, residual=False, trace=False, y=None, stream=None,
+                profile=False):
         import torch
         T = x.shape[0]
         if y is None:
@@ -189,9 +207,12 @@ class MoEContext:
             tx = torch.empty((layer_count, T, self.H), dtype=x.dtype, device=x.device)
             tid = torch.empty((layer_count, T, self.k), dtype=torch.int32, device=x.device)
             tw = torch.empty((layer_count, T, self.k), dtype=torch.float32, device=x.device)
-        moe_forward(self.handle, x, y, T, layer_begin, layer_count, MOE_FWD_RESIDUAL if residual else 0, tx, tid, tw,
-                    stream)
+        flags = (MOE_FWD_RESIDUAL if residual else 0) | (MOE_FWD_PROFILE if profile else 0)
+        moe_forward(self.handle, x, y, T, layer_begin, layer_count, flags, tx, tid, tw, stream)
         return (y, tx, tid, tw) if trace else y
+
+    def profile_read(self):
+        return moe_profile_read(self.handle)
 
     def memory_bytes(self):
         return moe_memory_bytes(self.handle)

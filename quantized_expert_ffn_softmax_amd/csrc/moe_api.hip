@@ -68,6 +68,9 @@ struct moe_ctx {
     uint8_t* dev_stage[2] = {nullptr, nullptr};
     hipEvent_t stage_done[2] = {nullptr, nullptr};
     uint64_t arena_bytes = 0;
+    // profiling: event pairs around kernel launches
+    std::vector<hipEvent_t> prof_events;
+    std::vector<moe_kernel_time> prof_recs;
 };
 
 namespace {
@@ -85,6 +88,7 @@ moe_status hip_fail(moe_ctx* c, hipError_t e, const char* what) {
 
 void free_ctx(moe_ctx* c) {
     if (!c) return;
+    for (hipEvent_t e : c->prof_events) hipEventDestroy(e);
     if (c->load_stream) hipStreamSynchronize(c->load_stream);
     for (int i = 0; i < 2; ++i) {
         if (c->host_stage[i]) hipHostFree(c->host_stage[i]);
@@ -105,7 +109,9 @@ moe_status check_config(const moe_config* cfg) {
         return fail(MOE_EINVAL, "abi_version %d, library is %d", cfg->abi_version, MOE_ABI_VERSION);
     if (cfg->hidden <= 0 || cfg->hidden % 32 || cfg->ffn <= 0 || cfg->ffn % 32)
         return fail(MOE_EINVAL, "hidden (%d) and ffn (%d) must be positive multiples of 32", cfg->hidden, cfg->ffn);
-    if (cfg->hidden > 65536 || cfg->ffn > 65536) return fail(MOE_EINVAL, "hidden/ffn above 65536");
+    // the decode kernels keep one 4096-wide row (gate/up) and one 2048-wide row (down) per workgroup pass
+    if (cfg->hidden > 4096 || cfg->ffn > 2048)
+        return fail(MOE_EINVAL, "hidden %d above 4096 or ffn %d above 2048", cfg->hidden, cfg->ffn);
     if (cfg->n_experts < 1 || cfg->n_experts > kMaxExperts)
         return fail(MOE_EINVAL, "n_experts %d outside [1, %d]", cfg->n_experts, kMaxExperts);
     if (cfg->n_shared != 0 && cfg->n_shared != 1) return fail(MOE_EINVAL, "n_shared must be 0 or 1");
@@ -192,6 +198,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     const size_t o_wtab = cv.take<float>((size_t)c->maxA * kMaxDecodeT);
     const size_t o_afrag = cv.take<uint32_t>((size_t)c->maxA * nbFp * 64 * 4);
     const size_t o_spart = cv.take<float>((size_t)c->maxA * nbFp * 32);
+    const size_t o_part = cv.take<float>((size_t)c->maxA * kMaxDecodeT * g.H);
     const size_t o_x0 = cv.take<uint16_t>((size_t)kMaxDecodeT * g.H);
     const size_t o_x1 = cv.take<uint16_t>((size_t)kMaxDecodeT * g.H);
     c->scratch_bytes = cv.off;
@@ -213,6 +220,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     c->rb.wtab = (float*)(b + o_wtab);
     c->db.afrag = (uint32_t*)(b + o_afrag);
     c->db.spart = (float*)(b + o_spart);
+    c->db.part = (float*)(b + o_part);
     c->xbuf[0] = (uint16_t*)(b + o_x0);
     c->xbuf[1] = (uint16_t*)(b + o_x1);
     if (hipMemset(c->scratch, 0, c->scratch_bytes) != hipSuccess ||
@@ -296,6 +304,30 @@ moe_status moe_load_experts(moe_ctx* c, const moe_layer_weights* w) {
 
 namespace {
 
+constexpr size_t kMaxProfiled = 65536;
+
+// Runs launch() between two recorded events when profiling is on.
+extern "C++" template <class F>
+moe_status timed(moe_ctx* c, bool prof, int kind, int layer, hipStream_t st, F launch, const char* what) {
+    size_t i = c->prof_recs.size();
+    prof = prof && i < kMaxProfiled;
+    if (prof) {
+        while (c->prof_events.size() < 2 * (i + 1)) {
+            hipEvent_t e;
+            HIP_TRY(c, hipEventCreate(&e));
+            c->prof_events.push_back(e);
+        }
+        HIP_TRY(c, hipEventRecord(c->prof_events[2 * i], st));
+    }
+    hipError_t e = launch();
+    if (e != hipSuccess) return hip_fail(c, e, what);
+    if (prof) {
+        HIP_TRY(c, hipEventRecord(c->prof_events[2 * i + 1], st));
+        c->prof_recs.push_back(moe_kernel_time{kind, layer, 0.f});
+    }
+    return MOE_OK;
+}
+
 moe_status check_layer_ready(moe_ctx* c, int layer, bool need_experts) {
     if (!c->router_loaded[layer]) return fail(MOE_ESTATE, "router of layer %d is not loaded", layer);
     if (need_experts) {
@@ -308,12 +340,15 @@ moe_status check_layer_ready(moe_ctx* c, int layer, bool need_experts) {
 }
 
 moe_status route_decode(moe_ctx* c, int layer, const uint16_t* x, int T, int32_t* trace_ids, float* trace_w,
-                        hipStream_t st) {
+                        hipStream_t st, bool prof = false) {
     const Geom& g = c->g;
-    HIP_TRY(c, launch_router_decode(x, T, c->routers + (size_t)layer * g.E * g.H, c->biases + (size_t)layer * g.E, g,
-                                    c->rb, st));
-    HIP_TRY(c, launch_topk_sort_decode(T, g, c->rb, trace_ids, trace_w, st));
-    return MOE_OK;
+    moe_status s = timed(c, prof, MOE_K_ROUTER, layer, st, [&] {
+        return launch_router_decode(x, T, c->routers + (size_t)layer * g.E * g.H, c->biases + (size_t)layer * g.E, g,
+                                    c->rb, st);
+    }, "router kernel launch");
+    if (s != MOE_OK) return s;
+    return timed(c, prof, MOE_K_TOPK_SORT, layer, st,
+                 [&] { return launch_topk_sort_decode(T, g, c->rb, trace_ids, trace_w, st); }, "top-k kernel launch");
 }
 
 }  // namespace
@@ -352,7 +387,7 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
         return fail(MOE_EINVAL, "layers [%d, %d) outside [0, %d)", a->layer_begin, a->layer_begin + a->layer_count, g.L);
     if (a->T < 0) return fail(MOE_EINVAL, "T %d is negative", a->T);
     if (a->T > c->cfg.max_tokens) return fail(MOE_ERANGE, "T %d above max_tokens %d", a->T, c->cfg.max_tokens);
-    if (a->flags & ~MOE_FWD_RESIDUAL) return fail(MOE_EINVAL, "unknown flags 0x%x", a->flags);
+    if (a->flags & ~(MOE_FWD_RESIDUAL | MOE_FWD_PROFILE)) return fail(MOE_EINVAL, "unknown flags 0x%x", a->flags);
     if (a->T == 0) return MOE_OK;
     if (!a->x || !a->y) return fail(MOE_EINVAL, "x and y are required");
     if (!aligned16(a->x) || !aligned16(a->y) || (a->trace_x && !aligned16(a->trace_x)))
@@ -375,14 +410,41 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
         uint16_t* yout = last ? (uint16_t*)a->y : c->xbuf[i & 1];
         if (a->trace_x)
             HIP_TRY(c, hipMemcpyAsync((uint8_t*)a->trace_x + (size_t)i * xbytes, xin, xbytes, hipMemcpyDeviceToDevice, st));
+        const bool prof = (a->flags & MOE_FWD_PROFILE) != 0;
         moe_status s = route_decode(c, l, xin, T, a->trace_ids ? a->trace_ids + (size_t)i * T * g.k : nullptr,
-                                    a->trace_w ? a->trace_w + (size_t)i * T * g.k : nullptr, st);
+                                    a->trace_w ? a->trace_w + (size_t)i * T * g.k : nullptr, st, prof);
         if (s != MOE_OK) return s;
         const uint8_t* slots = c->arena + (size_t)l * ES * g.slot_bytes;
-        HIP_TRY(c, launch_gateup_decode(xin, T, slots, g, c->rb, c->db, st));
-        HIP_TRY(c, launch_down_decode(xin, T, slots, g, c->rb, c->db, yout, a->flags & MOE_FWD_RESIDUAL, st));
+        s = timed(c, prof, MOE_K_GATEUP, l, st, [&] { return launch_gateup_decode(xin, T, slots, g, c->rb, c->db, st); },
+                  "gate/up kernel launch");
+        if (s != MOE_OK) return s;
+        s = timed(c, prof, MOE_K_DOWN, l, st, [&] { return launch_down_decode(T, slots, g, c->rb, c->db, st); },
+                  "down kernel launch");
+        if (s != MOE_OK) return s;
+        s = timed(c, prof, MOE_K_COMBINE, l, st, [&] {
+            return launch_combine_decode(xin, T, g, c->rb, c->db, yout, a->flags & MOE_FWD_RESIDUAL, st);
+        }, "combine kernel launch");
+        if (s != MOE_OK) return s;
         xin = yout;
     }
+    return MOE_OK;
+}
+
+moe_status moe_profile_read(moe_ctx* c, moe_kernel_time* out, int32_t cap, int32_t* n_out) {
+    if (!c || !n_out || (cap > 0 && !out)) return fail(MOE_EINVAL, "ctx, out or n_out is NULL");
+    if (c->poisoned) return fail(MOE_ESTATE, "context is poisoned by an earlier HIP failure");
+    const size_t n = c->prof_recs.size();
+    *n_out = 0;
+    if (n) HIP_TRY(c, hipEventSynchronize(c->prof_events[2 * n - 1]));
+    int32_t w = 0;
+    for (size_t i = 0; i < n && w < cap; ++i, ++w) {
+        float ms = 0.f;
+        HIP_TRY(c, hipEventElapsedTime(&ms, c->prof_events[2 * i], c->prof_events[2 * i + 1]));
+        out[w] = c->prof_recs[i];
+        out[w].ms = ms;
+    }
+    *n_out = w;
+    c->prof_recs.clear();
     return MOE_OK;
 }
 

@@ -85,7 +85,7 @@ inline Geom make_geom(int H, int F, int E, int S, int k, int fmt, int L) {
 // Per-call routing scratch (device), sized for max_tokens by the runtime.
 struct RouteBufs {
     double* logits;   // [T x E]
-    float* sx;        // [nbH x 16] per-block sums of x rows (decode path)
+    float* sx;        // [nbH_pad x 16] per-block sums of the x rows (rows >= T zero)
     int32_t* ids;     // [T x k]
     float* w;         // [T x k]
     int32_t* offsets; // [E + 1]
@@ -98,9 +98,12 @@ struct RouteBufs {
 
 // Decode FFN scratch.
 struct DecodeBufs {
-    uint32_t* afrag;  // [maxA x nbF_pad x 64 x 4] bf16 pairs, down-projection A operand
-    float* spart;     // [maxA x nbF_pad x 2 x 16] per-half-block sums of afrag rows
+    uint32_t* afrag;  // [maxA x nbF_pad x 64 x 4] v = w*SwiGLU as bf16 hi/lo MFMA A fragments
+    float* spart;     // [maxA x nbF_pad x 2 x 16] per-half-block sums of the fragment rows
+    float* part;      // [maxA x 8 x H] per-expert down projections
 };
+
+constexpr int kDownRowsPerWG = 128;  // 8 waves x 16 rows
 
 // Launchers (return hipGetLastError()).
 hipError_t launch_repack(const uint8_t* canon, uint8_t* slots, int count, const Geom& g, hipStream_t st);
@@ -110,7 +113,9 @@ hipError_t launch_topk_sort_decode(int T, const Geom& g, RouteBufs rb, int32_t* 
                                    hipStream_t st);
 hipError_t launch_gateup_decode(const uint16_t* x, int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb,
                                 DecodeBufs db, hipStream_t st);
-hipError_t launch_down_decode(const uint16_t* x, int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb,
-                              DecodeBufs db, uint16_t* y, int residual, hipStream_t st);
+hipError_t launch_down_decode(int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb, DecodeBufs db,
+                              hipStream_t st);
+hipError_t launch_combine_decode(const uint16_t* x, int T, const Geom& g, RouteBufs rb, DecodeBufs db, uint16_t* y,
+                                 int residual, hipStream_t st);
 
 }  // namespace moe

@@ -1,18 +1,22 @@
 // Decode-path kernels of the MI355X sparse-MoE layer (gfx950, wave64).
 //
-// Per layer and call (T <= 8 tokens):
+// Per layer and call (T <= 8 tokens), five launches:
 //   k_router_decode   router GEMV (+bias) with fp64 accumulation of the exact
 //                     bf16 x bf16 products; also the per-block sums of x
-//   k_topk_sort       one workgroup: wave top-k per token (logit descending,
-//                     lower id on ties), renormalised softmax weights, stable
-//                     counting sort of the (token, expert) pairs, the list of
-//                     active experts and the per-(expert, token) weight table
+//   k_topk_sort       one workgroup: top-k per token (logit descending, lower
+//                     id on ties; DPP wave arg-max), renormalised softmax
+//                     weights, stable counting sort of the (token, expert)
+//                     pairs from per-expert token bitmasks, active-expert list
+//                     and weight table
 //   k_gateup_decode   per (active expert, 16-row tile of F): fused dequant +
-//                     gate/up GEMV on bf16 MFMA + SwiGLU; writes w*h split
-//                     into bf16 hi/lo halves as the down projection's operand
-//   k_down_decode     per 16-row tile of H: down GEMV over all active experts
-//                     in ascending order, atomic-free weighted combine,
-//                     optional residual, bf16 output
+//                     gate/up GEMV on bf16 MFMA + SwiGLU; weights and x
+//                     fragments stream through a 4-chunk prefetch ring; writes
+//                     v = w * SwiGLU as bf16 hi/lo halves in MFMA-operand order
+//   k_down_decode     per (active expert, 128-row group of H): down GEMV with
+//                     the expert's operand staged once in LDS; stores one
+//                     partial row block per expert
+//   k_combine_decode  sums the experts in ascending active order (no atomics,
+//                     deterministic), adds the residual, writes bf16
 //
 // Method references (pages): sparse top-k routing with a shared expert and
 // gate/up/down expert tensors -- "Strata 改源码去跑 DeepSeek V4 Flash？",
@@ -185,44 +189,159 @@ hipError_t launch_repack(const uint8_t* canon, uint8_t* slots, int count, const 
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- wave helpers
+// DPP lane permutations (GFX9 encodings): quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror.  Applied in this order, followed by xor 16 and
+// xor 32, every lane ends up combined with every other lane of the wave.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL> __device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL> __device__ __forceinline__ double dpp_f64(double v) {
+    const int lo = dpp<CTRL>(__double2loint(v)), hi = dpp<CTRL>(__double2hiint(v));
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v += dpp_f64<kDppXor1>(v);
+    v += dpp_f64<kDppXor2>(v);
+    v += dpp_f64<kDppHalfMirror>(v);
+    v += dpp_f64<kDppMirror>(v);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Total order of doubles as unsigned keys (-0 folded into +0).
+__device__ __forceinline__ uint64_t order_key(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v + 0.0);
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+__device__ __forceinline__ double key_value(uint64_t k) {
+    const uint64_t u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+    return __longlong_as_double((long long)u);
+}
+// (key, id) ordering of the selection: larger logit first, lower id on equal logits
+__device__ __forceinline__ bool ahead(uint64_t k1, int e1, uint64_t k2, int e2) {
+    return k1 > k2 || (k1 == k2 && e1 < e2);
+}
+template <int CTRL> __device__ __forceinline__ void argmax_step(uint64_t& k, int& e) {
+    const uint32_t lo = (uint32_t)dpp<CTRL>((int)(uint32_t)k);
+    const uint32_t hi = (uint32_t)dpp<CTRL>((int)(uint32_t)(k >> 32));
+    const int oe = dpp<CTRL>(e);
+    const uint64_t ok = ((uint64_t)hi << 32) | lo;
+    if (ahead(ok, oe, k, e)) { k = ok; e = oe; }
+}
+template <int CTRL, int ROWS> __device__ __forceinline__ void argmax_bcast(uint64_t& k, int& e) {
+    // lanes outside ROWS keep their own value (old = own), so the compare is a no-op there
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)k, (int)(uint32_t)k, CTRL, ROWS, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(k >> 32), (int)(uint32_t)(k >> 32), CTRL,
+                                                              ROWS, 0xF, false);
+    const int oe = __builtin_amdgcn_update_dpp(e, e, CTRL, ROWS, 0xF, false);
+    const uint64_t ok = ((uint64_t)hi << 32) | lo;
+    if (ahead(ok, oe, k, e)) { k = ok; e = oe; }
+}
+// Wave-wide best (key, id): row-level DPP butterflies, then row_bcast:15 and
+// row_bcast:31 carry the row winners into lane 63, which is read back as a
+// wave-uniform value.  Only VALU/DPP operations, no LDS round trips.
+__device__ __forceinline__ void wave_argmax(uint64_t& k, int& e) {
+    argmax_step<kDppXor1>(k, e);
+    argmax_step<kDppXor2>(k, e);
+    argmax_step<kDppHalfMirror>(k, e);
+    argmax_step<kDppMirror>(k, e);
+    argmax_bcast<0x142, 0xA>(k, e);  // row_bcast:15 into rows 1 and 3
+    argmax_bcast<0x143, 0xC>(k, e);  // row_bcast:31 into rows 2 and 3
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
+    e = __builtin_amdgcn_readlane(e, 63);
+    k = ((uint64_t)hi << 32) | lo;
+}
+
+// Raise a kernel's dynamic LDS limit when a launch needs more than the default.
+template <class K> hipError_t ensure_lds(K kernel, int bytes, int& granted) {
+    if (bytes <= granted) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) granted = bytes;
+    return e;
+}
+
+// Copy n16 16-byte elements from global memory to LDS with the whole
+// workgroup; every thread issues up to 8 loads before its first LDS store, so
+// the copy costs one memory latency.  dst_index maps a source element index
+// to its LDS element index (row padding).
+template <class Map>
+__device__ __forceinline__ void stage_lds(u32x4_t* dst, const u32x4_t* __restrict__ src, int n16, Map dst_index) {
+    for (int i0 = threadIdx.x; i0 < n16; i0 += blockDim.x * 8) {
+        u32x4_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = i0 + j * (int)blockDim.x;
+            if (i < n16) v[j] = src[i];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = i0 + j * (int)blockDim.x;
+            if (i < n16) dst[dst_index(i)] = v[j];
+        }
+    }
+}
+
 // ---------------------------------------------------------------- router
-// logits[t][e] = sum_h x[t][h] * Wr[e][h] + b[e]: every bf16 x bf16 product is
-// exact in fp32 and is accumulated in fp64 (fixed reduction tree), so the
-// selection agrees with an fp64 evaluation except at logit gaps near 1e-15.
-// Grid: ceil(E/2) workgroups of 4 waves; waves (0,1) -> expert 2b, (2,3) ->
-// expert 2b+1; the two waves of an expert split H in halves.
-// Workgroup 0 also writes sx[b][m] = sum of x[m][32b..32b+31] (fp32, m < T,
-// zero elsewhere), the per-block sums used to remove the operand offset.
+// Grid ceil(E/4) workgroups of 4 waves; wave w of workgroup b computes the
+// logits of expert 4b+w for every token.  Every bf16 x bf16 product is exact
+// in fp32 and is accumulated in fp64 (fixed reduction tree), so the selection
+// agrees with an fp64 evaluation except at logit gaps near 1e-15.
+// Each wave first issues all loads of its router row (up to 8 x 16 bytes per
+// lane per pass) while the workgroup stages x in LDS; one wait, then math.
+// All threads of the grid also share the per-block sums
+// sx[b][m] = sum_{q<32} x[m][32b+q] (fp32, in q order; zero for m >= T).
+constexpr int kRouterPass = 8;  // 16-byte loads per lane per pass: H <= 4096 in one pass
+
 __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restrict__ x, int T,
                                                        const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
                                                        int E, int H, int nbp, double* __restrict__ logits,
                                                        float* __restrict__ sx) {
-    __shared__ double part[4][kMaxDecodeT];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int e = blockIdx.x * 2 + (wave >> 1);
-    const int half = wave & 1;
-    const int Hh = H / 2;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [T][H]
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int e = blockIdx.x * 4 + wave;
+    const uint16_t* wrow = Wr + (int64_t)(e < E ? e : E - 1) * H;
+    const double be = bias ? (double)bias[e < E ? e : E - 1] : 0.0;
     double acc[kMaxDecodeT];
 #pragma unroll
     for (int t = 0; t < kMaxDecodeT; ++t) acc[t] = 0.0;
-    if (e < E) {
-        const uint16_t* wrow = Wr + (int64_t)e * H + half * Hh;
-        for (int h0 = lane * 8; h0 < Hh; h0 += 512) {
-            const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(wrow + h0);
-            float wf[8];
+    for (int p0 = 0; p0 < H; p0 += 512 * kRouterPass) {
+        u32x4_t wv[kRouterPass];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                wf[2 * q] = __uint_as_float(wv[q] << 16);
-                wf[2 * q + 1] = __uint_as_float(wv[q] & 0xFFFF0000u);
-            }
+        for (int j = 0; j < kRouterPass; ++j) {
+            const int h0 = p0 + (lane + 64 * j) * 8;
+            wv[j] = h0 < H ? *reinterpret_cast<const u32x4_t*>(wrow + h0) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+        if (p0 == 0) {
+            stage_lds(reinterpret_cast<u32x4_t*>(xs), reinterpret_cast<const u32x4_t*>(x), T * (H / 8),
+                      [](int i) { return i; });
+            __syncthreads();
+        }
 #pragma unroll
-            for (int t = 0; t < kMaxDecodeT; ++t) {
-                if (t < T) {
-                    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(x + (int64_t)t * H + half * Hh + h0);
+        for (int j = 0; j < kRouterPass; ++j) {
+            const int h0 = p0 + (lane + 64 * j) * 8;
+            if (h0 < H) {
+                float wf[8];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[t] += (double)(__uint_as_float(xv[q] << 16) * wf[2 * q]);
-                        acc[t] += (double)(__uint_as_float(xv[q] & 0xFFFF0000u) * wf[2 * q + 1]);
+                for (int q = 0; q < 4; ++q) {
+                    wf[2 * q] = __uint_as_float(wv[j][q] << 16);
+                    wf[2 * q + 1] = __uint_as_float(wv[j][q] & 0xFFFF0000u);
+                }
+#pragma unroll
+                for (int t = 0; t < kMaxDecodeT; ++t) {
+                    if (t < T) {
+                        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs + t * H + h0);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            acc[t] += (double)(__uint_as_float(xv[q] << 16) * wf[2 * q]);
+                            acc[t] += (double)(__uint_as_float(xv[q] & 0xFFFF0000u) * wf[2 * q + 1]);
+                        }
                     }
                 }
             }
@@ -230,347 +349,516 @@ __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restric
     }
 #pragma unroll
     for (int t = 0; t < kMaxDecodeT; ++t) {
-        double v = acc[t];
-        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-        if (lane == 0) part[wave][t] = v;
-    }
-    __syncthreads();
-    if (threadIdx.x < 2 * kMaxDecodeT) {
-        const int pair = threadIdx.x / kMaxDecodeT, t = threadIdx.x % kMaxDecodeT;
-        const int ee = blockIdx.x * 2 + pair;
-        if (ee < E && t < T)
-            logits[(int64_t)t * E + ee] = (part[2 * pair][t] + part[2 * pair + 1][t]) + (bias ? (double)bias[ee] : 0.0);
-    }
-    if (blockIdx.x == 0) {
-        const int nb = H / 32;
-        for (int i = threadIdx.x; i < nbp * 16; i += blockDim.x) {
-            const int b = i >> 4, m = i & 15;
-            float s = 0.f;
-            if (m < T && b < nb) {
-                const uint16_t* xr = x + (int64_t)m * H + b * 32;
-                for (int q = 0; q < 32; ++q) s += bf2f(xr[q]);
-            }
-            sx[i] = s;
+        if (t < T) {
+            const double v = wave_sum_f64(acc[t]);
+            if (lane == 0 && e < E) logits[(int64_t)t * E + e] = v + be;
         }
+    }
+    const int nb = H / 32;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nbp * 16; i += gridDim.x * blockDim.x) {
+        const int b = i >> 4, m = i & 15;
+        float s = 0.f;
+        if (m < T && b < nb) {
+            const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(xs + m * H + b * 32);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const u32x4_t v = xr[r];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    s += __uint_as_float(v[q] << 16);
+                    s += __uint_as_float(v[q] & 0xFFFF0000u);
+                }
+            }
+        }
+        sx[i] = s;
     }
 }
 
 hipError_t launch_router_decode(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const Geom& g,
                                 RouteBufs rb, hipStream_t st) {
-    hipLaunchKernelGGL(k_router_decode, dim3((g.E + 1) / 2), dim3(256), 0, st, x, T, Wr, bias, g.E, g.H,
+    static int granted = 64 * 1024;
+    const int lds = T * g.H * 2;
+    hipError_t e = ensure_lds(k_router_decode, lds, granted);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_router_decode, dim3((g.E + 3) / 4), dim3(256), lds, st, x, T, Wr, bias, g.E, g.H,
                        g.gu.nch * 4, rb.logits, rb.sx);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- top-k + sort
-// One workgroup of 512 threads; wave t handles token t (T <= 8).
-__global__ __launch_bounds__(512) void k_topk_sort(int T, int E, int k, int S, const double* __restrict__ logits,
-                                                   int32_t* __restrict__ ids, float* __restrict__ wout,
-                                                   int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-                                                   int32_t* __restrict__ inv, int32_t* __restrict__ nact,
-                                                   int32_t* __restrict__ act, float* __restrict__ wtab,
+// One workgroup of 4 waves; wave w routes tokens w and w+4.  The counting
+// sort uses one bitmask of tokens per expert: the pairs of a token have
+// distinct experts, so the rank of pair (t, j) inside the group of expert e is
+// the number of tokens t' < t that chose e, and the group size is popc(mask).
+template <int J>
+__global__ __launch_bounds__(256) void k_topk_sort(int T, int E, int k, int S, RouteBufs rb,
                                                    int32_t* __restrict__ trace_ids, float* __restrict__ trace_w) {
+    __shared__ uint32_t s_mask[kMaxExperts];
+    __shared__ int32_t s_off[kMaxExperts];
+    __shared__ int32_t s_aidx[kMaxExperts];
     __shared__ int32_t s_ids[kMaxDecodeT * kMaxTopK];
     __shared__ float s_w[kMaxDecodeT * kMaxTopK];
-    __shared__ uint32_t s_cnt[kMaxExperts];
-    __shared__ uint32_t s_wavesum[8];
-    __shared__ int32_t s_aidx[kMaxExperts];
-    __shared__ int32_t s_off[kMaxExperts];
     __shared__ float s_wtab[(kMaxDecodeT * kMaxTopK + 1) * kMaxDecodeT];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ uint32_t s_wsum[4];
+    __shared__ int s_U;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int P = T * k;
+    // logits of this wave's tokens (t = wave, wave + 4) are requested first
+    // (unconditional loads with clamped indices: all of them are in flight together)
+    double raw[2][J];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int t = min(wave + 4 * r, T - 1);
+#pragma unroll
+        for (int j = 0; j < J; ++j) raw[r][j] = rb.logits[(int64_t)t * E + min(lane + 64 * j, E - 1)];
+    }
+    for (int e = tid; e < E; e += blockDim.x) s_mask[e] = 0u;
+    for (int i = tid; i < (P + S) * kMaxDecodeT; i += blockDim.x) s_wtab[i] = 0.f;
+    __syncthreads();
 
-    if (wave < T) {
-        const int t = wave;
-        constexpr int J = kMaxExperts / 64;
-        double v[J];
-        bool taken[J];
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2) {
+        const int t = wave + 4 * r2;
+        if (t >= T) break;
+        uint64_t key[J];
+        uint32_t taken = 0;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int e = lane + 64 * j;
-            v[j] = e < E ? logits[(int64_t)t * E + e] : -__builtin_huge_val();
-            taken[j] = e >= E;
+            key[j] = lane + 64 * j < E ? order_key(raw[r2][j]) : 0ull;
+            if (lane + 64 * j >= E) taken |= 1u << j;
         }
-        double sel_v0 = 0.0, my_v = 0.0;
+        uint64_t my_k = 0, k0 = 0;
         int my_e = 0;
         for (int r = 0; r < k; ++r) {
-            double bv = -__builtin_huge_val();
+            uint64_t bk = 0;
             int be = 0x7FFFFFFF;
 #pragma unroll
-            for (int j = 0; j < J; ++j) {
-                const int e = lane + 64 * j;
-                if (!taken[j] && (v[j] > bv || (v[j] == bv && e < be))) { bv = v[j]; be = e; }
-            }
-            for (int off = 32; off > 0; off >>= 1) {
-                const double ov = __shfl_xor(bv, off);
-                const int oe = __shfl_xor(be, off);
-                if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-            }
-            if ((be & 63) == lane) {
-#pragma unroll
-                for (int j = 0; j < J; ++j)
-                    if (lane + 64 * j == be) taken[j] = true;
-            }
-            if (r == 0) sel_v0 = bv;
-            if (lane == r) { my_v = bv; my_e = be; }
+            for (int j = 0; j < J; ++j)
+                if (!((taken >> j) & 1u) && ahead(key[j], lane + 64 * j, bk, be)) { bk = key[j]; be = lane + 64 * j; }
+            wave_argmax(bk, be);
+            if ((be & 63) == lane) taken |= 1u << (be >> 6);
+            if (r == 0) k0 = bk;
+            if (lane == r) { my_k = bk; my_e = be; }
         }
-        // renormalised softmax over the k selected logits (fp64)
-        const double ex = lane < k ? exp(my_v - sel_v0) : 0.0;
-        double z = ex;
-        for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+        // renormalised softmax over the selected logits (fp64)
+        const double ex = lane < k ? exp(key_value(my_k) - key_value(k0)) : 0.0;
+        const double z = wave_sum_f64(ex);
         if (lane < k) {
             const float wv = (float)(ex / z);
             s_ids[t * k + lane] = my_e;
             s_w[t * k + lane] = wv;
-            ids[t * k + lane] = my_e;
-            wout[t * k + lane] = wv;
+            atomicOr(&s_mask[my_e], 1u << t);
+            rb.ids[t * k + lane] = my_e;
+            rb.w[t * k + lane] = wv;
             if (trace_ids) trace_ids[t * k + lane] = my_e;
             if (trace_w) trace_w[t * k + lane] = wv;
         }
     }
-    for (int e = threadIdx.x; e < kMaxExperts; e += blockDim.x) s_cnt[e] = 0;
     __syncthreads();
-    if (threadIdx.x < P) atomicAdd(&s_cnt[s_ids[threadIdx.x]], 1u);
-    __syncthreads();
-    // exclusive scan of packed (count << 16 | nonempty) over E <= 1024 entries, 2 per thread
-    const int e0 = 2 * threadIdx.x;
-    const uint32_t c0 = e0 < E ? s_cnt[e0] : 0u, c1 = e0 + 1 < E ? s_cnt[e0 + 1] : 0u;
-    const uint32_t p0 = (c0 << 16) | (c0 ? 1u : 0u), p1 = (c1 << 16) | (c1 ? 1u : 0u);
-    uint32_t incl = p0 + p1;
+    // exclusive scan over experts of (pairs << 16 | non-empty), 4 experts per thread
+    uint32_t p[4], tot = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = tid * 4 + j;
+        const uint32_t mk = e < E ? s_mask[e] : 0u;
+        p[j] = ((uint32_t)__popc(mk) << 16) | (mk ? 1u : 0u);
+        tot += p[j];
+    }
+    uint32_t incl = tot;
     for (int off = 1; off < 64; off <<= 1) {
         const uint32_t o = __shfl_up(incl, off);
         if (lane >= off) incl += o;
     }
-    if (lane == 63) s_wavesum[wave] = incl;
+    if (lane == 63) s_wsum[wave] = incl;
     __syncthreads();
-    uint32_t base = 0;
-    for (int w = 0; w < wave; ++w) base += s_wavesum[w];
-    const uint32_t ex0 = base + incl - (p0 + p1);
-    const uint32_t ex1 = ex0 + p0;
-    if (e0 < E) {
-        offsets[e0] = s_off[e0] = (int32_t)(ex0 >> 16);
-        s_aidx[e0] = (int32_t)(ex0 & 0xFFFFu);
-        if (c0) act[ex0 & 0xFFFFu] = e0;
+    uint32_t ex = incl - tot;
+    for (int w = 0; w < wave; ++w) ex += s_wsum[w];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = tid * 4 + j;
+        if (e < E) {
+            rb.offsets[e] = s_off[e] = (int32_t)(ex >> 16);
+            s_aidx[e] = (int32_t)(ex & 0xFFFFu);
+        }
+        ex += p[j];
     }
-    if (e0 + 1 < E) {
-        offsets[e0 + 1] = s_off[e0 + 1] = (int32_t)(ex1 >> 16);
-        s_aidx[e0 + 1] = (int32_t)(ex1 & 0xFFFFu);
-        if (c1) act[ex1 & 0xFFFFu] = e0 + 1;
+    if (tid == (int)blockDim.x - 1) {  // entries past E add nothing: ex is the grand total
+        rb.offsets[E] = (int32_t)(ex >> 16);
+        s_U = (int32_t)(ex & 0xFFFFu);
     }
-    uint32_t total = 0;
-    for (int w = 0; w < 8; ++w) total += s_wavesum[w];
-    const int U = (int)(total & 0xFFFFu);
-    const int nA = U + S;
-    if (threadIdx.x == 0) {
-        offsets[E] = P;
-        nact[0] = nA;
-        if (S) act[U] = E;
-    }
-    for (int i = threadIdx.x; i < nA * kMaxDecodeT; i += blockDim.x) s_wtab[i] = 0.f;
     __syncthreads();
-    if (threadIdx.x < P) {
-        const int i = threadIdx.x, e = s_ids[i];
-        int rank = 0;
-        for (int q = 0; q < i; ++q) rank += s_ids[q] == e;
+    const int U = s_U;
+    if (tid < P) {
+        const int t = tid / k, e = s_ids[tid];
+        const int rank = __popc(s_mask[e] & ((1u << t) - 1u));
         const int pos = s_off[e] + rank;
-        perm[pos] = i;
-        inv[i] = pos;
-        s_wtab[s_aidx[e] * kMaxDecodeT + i / k] = s_w[i];
+        rb.perm[pos] = tid;
+        rb.inv[tid] = pos;
+        const int a = s_aidx[e];
+        if (rank == 0) rb.act[a] = e;
+        s_wtab[a * kMaxDecodeT + t] = s_w[tid];
     }
-    if (S && threadIdx.x < T) s_wtab[U * kMaxDecodeT + threadIdx.x] = 1.0f;
+    if (tid == 0) {
+        rb.nact[0] = U + S;
+        if (S) rb.act[U] = E;
+    }
+    if (S && tid < T) s_wtab[U * kMaxDecodeT + tid] = 1.0f;
     __syncthreads();
-    for (int i = threadIdx.x; i < nA * kMaxDecodeT; i += blockDim.x) wtab[i] = s_wtab[i];
+    for (int i = tid; i < (U + S) * kMaxDecodeT; i += blockDim.x) rb.wtab[i] = s_wtab[i];
 }
 
 hipError_t launch_topk_sort_decode(int T, const Geom& g, RouteBufs rb, int32_t* trace_ids, float* trace_w,
                                    hipStream_t st) {
-    hipLaunchKernelGGL(k_topk_sort, dim3(1), dim3(512), 0, st, T, g.E, g.k, g.S, rb.logits, rb.ids, rb.w, rb.offsets,
-                       rb.perm, rb.inv, rb.nact, rb.act, rb.wtab, trace_ids, trace_w);
+    if (g.E <= 256)
+        hipLaunchKernelGGL(k_topk_sort<4>, dim3(1), dim3(256), 0, st, T, g.E, g.k, g.S, rb, trace_ids, trace_w);
+    else if (g.E <= 512)
+        hipLaunchKernelGGL(k_topk_sort<8>, dim3(1), dim3(256), 0, st, T, g.E, g.k, g.S, rb, trace_ids, trace_w);
+    else
+        hipLaunchKernelGGL(k_topk_sort<16>, dim3(1), dim3(256), 0, st, T, g.E, g.k, g.S, rb, trace_ids, trace_w);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- gate/up + SwiGLU
-// Grid (F/16, maxA), 256 threads.  Workgroup (rt, a): rows 16rt..16rt+15 of G
-// and U of active expert a; the 4 waves split K = H by chunks.  The MFMA
-// computes C[m = token][n = row] with A = x (rows m >= T are zero).
-template <int FMT>
+// Persistent grid.  A work item is (active expert a, 16-row tile rt of F):
+// rows 16rt..16rt+15 of G and U.  The 4 waves of a workgroup split K = H into
+// contiguous ranges of at most NC chunks.  x is staged in LDS once per
+// workgroup.  Every wave keeps one register slot per chunk of its range: while
+// chunk j of the current item is multiplied, chunk j of the workgroup's next
+// item is requested into the same slot, so loads of one item overlap the
+// MFMAs of the previous one.  Loads are unconditional (indices clamped) so the
+// compiler can count them.  The MFMA computes C[m = token][n = row] with
+// A = x (rows m >= T zero).  Output: v = w_t,a * silu(g) * u as the bf16
+// hi/lo A fragments of the down projection, and their per-half-block sums.
+template <int FMT, int NC>
 __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restrict__ x, int T,
                                                        const uint8_t* __restrict__ slots, Geom g,
                                                        const float* __restrict__ sx, const int32_t* __restrict__ nact,
                                                        const int32_t* __restrict__ act, const float* __restrict__ wtab,
                                                        uint32_t* __restrict__ afrag, float* __restrict__ spart) {
-    __shared__ f32x4_t red[4][4][64];
-    const int a = blockIdx.y;
-    if (a >= nact[0]) return;
-    const int rt = blockIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int rtn = g.F / 16;
+    const int items = nact[0] * rtn;
+    if ((int)blockIdx.x >= items) return;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, gs = lane >> 4, m = lane & 15;
-    const int e = act[a];
     const MatGeom& mg = g.gu;
-    const uint8_t* Gt = slots + (int64_t)e * g.slot_bytes + g.g_off + (int64_t)rt * mg.tile_bytes;
-    const uint8_t* Ut = slots + (int64_t)e * g.slot_bytes + g.u_off + (int64_t)rt * mg.tile_bytes;
     const int c0 = wave * mg.nch / 4, c1 = (wave + 1) * mg.nch / 4;
-    const bool xrow = m < T;
-    const uint16_t* xr = x + (int64_t)m * g.H + 8 * gs;
-    f32x4_t accG = {0.f, 0.f, 0.f, 0.f}, accU = accG, corG = accG, corU = accG;
-    for (int c = c0; c < c1; ++c) {
-        uint32_t cg[4], cu[4];
-        load_codes<FMT>(Gt + (int64_t)c * mg.chunk_bytes, lane, cg);
-        load_codes<FMT>(Ut + (int64_t)c * mg.chunk_bytes, lane, cu);
-        const u32x2_t sg = load_scales(Gt + (int64_t)c * mg.chunk_bytes, QF<FMT>::kCW, n);
-        const u32x2_t su = load_scales(Ut + (int64_t)c * mg.chunk_bytes, QF<FMT>::kCW, n);
-        u32x4_t A[4];
+    constexpr int CWN = FMT == 1 ? 4 : 2;
+    const int xstride = g.H + 8;
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [T][H + 8] (rows padded against bank conflicts)
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem + ((T * xstride * 2 + 15) / 16) * 16);  // [2][3][4][64]
+    __shared__ int32_t s_act[kMaxDecodeT * kMaxTopK + 1];
+    __shared__ float s_wt[(kMaxDecodeT * kMaxTopK + 1) * kMaxDecodeT];
+
+    uint32_t cg[NC][CWN], cu[NC][CWN];
+    u32x2_t sg[NC], su[NC];
+    float sxv[NC];
+    auto tiles = [&](int e, int rt, const uint8_t*& Gt, const uint8_t*& Ut) {
+        const int64_t base = (int64_t)e * g.slot_bytes + (int64_t)rt * mg.tile_bytes;
+        Gt = slots + base + g.g_off;
+        Ut = slots + base + g.u_off;
+    };
+    auto load = [&](const uint8_t* Gt, const uint8_t* Ut, int j) {
+        const int c = min(c0 + j, mg.nch - 1);
+        const int64_t off = (int64_t)c * mg.chunk_bytes;
+        load_codes<FMT>(Gt + off, lane, cg[j]);
+        load_codes<FMT>(Ut + off, lane, cu[j]);
+        sg[j] = load_scales(Gt + off, QF<FMT>::kCW, n);
+        su[j] = load_scales(Ut + off, QF<FMT>::kCW, n);
+        sxv[j] = sx[(c * 4 + gs) * 16 + m];
+    };
+    int it = blockIdx.x;
+    const uint8_t *Gt, *Ut;
+    tiles(act[it / rtn], it % rtn, Gt, Ut);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int b = c * 4 + j;
-            A[j] = (xrow && b < mg.nb) ? *reinterpret_cast<const u32x4_t*>(xr + b * 32) : u32x4_t{0u, 0u, 0u, 0u};
-        }
-        const float s = sx[(c * 4 + gs) * 16 + m];
-        chunk_mac<FMT>(cg, sg, A, s, gs, accG, corG);
-        chunk_mac<FMT>(cu, su, A, s, gs, accU, corU);
+    for (int j = 0; j < NC; ++j) load(Gt, Ut, j);
+    {
+        const int nA = nact[0];
+        for (int i = threadIdx.x; i < nA; i += blockDim.x) s_act[i] = act[i];
+        for (int i = threadIdx.x; i < nA * kMaxDecodeT; i += blockDim.x) s_wt[i] = wtab[i];
+        const int h8 = g.H / 8, xs8 = xstride / 8;
+        stage_lds(reinterpret_cast<u32x4_t*>(xs), reinterpret_cast<const u32x4_t*>(x), T * h8, [=](int q) {
+            const int t = q / h8;
+            return t * xs8 + (q - t * h8);
+        });
     }
-    red[wave][0][lane] = accG;
-    red[wave][1][lane] = accU;
-    red[wave][2][lane] = corG;
-    red[wave][3][lane] = corU;
     __syncthreads();
-    if (wave != 0) return;
-    f32x4_t sG = red[0][0][lane], sU = red[0][1][lane], qG = red[0][2][lane], qU = red[0][3][lane];
-    for (int w = 1; w < 4; ++w) {
-        sG += red[w][0][lane];
-        sU += red[w][1][lane];
-        qG += red[w][2][lane];
-        qU += red[w][3][lane];
-    }
-    // lane holds (token t = 4*gs + i, row f = 16*rt + n); tokens < 8 live in gs 0..1
-    const int nbFp = g.dn.nch * 4;
-    const int bF = rt >> 1, kf0 = 16 * (rt & 1);
-    const int kf = kf0 + n;
-    uint16_t* af16 = reinterpret_cast<uint16_t*>(afrag) + ((int64_t)a * nbFp + bF) * 64 * 8;
-    float shi[4], slo[4];
+    const bool xrow = m < T;
+    const uint16_t* xl = xs + m * xstride + 8 * gs;
+    int buf = 0;
+    for (; it < items; it += gridDim.x, buf ^= 1) {
+        const int a = it / rtn, rt = it - a * rtn;
+        const int nx = it + (int)gridDim.x < items ? it + (int)gridDim.x : it;
+        const uint8_t *Gn, *Un;
+        tiles(s_act[nx / rtn], nx % rtn, Gn, Un);
+        f32x4_t accG = {0.f, 0.f, 0.f, 0.f}, accU = accG, corG = accG, corU = accG;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = 4 * gs + i;
-        const float gv = sG[i] - QF<FMT>::kBias * qG[i];
-        const float uv = sU[i] - QF<FMT>::kBias * qU[i];
-        const float h = gv / (1.0f + expf(-gv)) * uv;
-        const float wt = t < kMaxDecodeT ? wtab[a * kMaxDecodeT + t] : 0.f;
-        const float v = wt * h;
-        const uint32_t hi = f2bf(v);
-        const uint32_t lo = f2bf(v - bf2f(hi));
-        shi[i] = bf2f(hi);
-        slo[i] = bf2f(lo);
-        if (t < T) {
-            af16[(t + 16 * (kf >> 3)) * 8 + (kf & 7)] = (uint16_t)hi;
-            af16[(8 + t + 16 * (kf >> 3)) * 8 + (kf & 7)] = (uint16_t)lo;
+        for (int j = 0; j < NC; ++j) {
+            const int c = c0 + j;
+            if (c < c1) {
+                u32x4_t A[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int b = c * 4 + q;
+                    A[q] = (xrow && b < mg.nb) ? *reinterpret_cast<const u32x4_t*>(xl + b * 32) : u32x4_t{0u, 0u, 0u, 0u};
+                }
+                chunk_mac<FMT>(cg[j], sg[j], A, sxv[j], gs, accG, corG);
+                chunk_mac<FMT>(cu[j], su[j], A, sxv[j], gs, accU, corU);
+            }
+            load(Gn, Un, j);  // chunk j of the next item (a repeat of this one after the last item)
         }
-    }
-    // per-half-block row sums of the operand halves, reduced over the 16 rows n of this lane group
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        for (int off = 1; off < 16; off <<= 1) {
-            shi[i] += __shfl_xor(shi[i], off);
-            slo[i] += __shfl_xor(slo[i], off);
+        // waves 1..3 hand their partial sums to wave 0 (double-buffered: one barrier per item)
+        f32x4_t* rb2 = red + buf * 3 * 4 * 64;
+        if (wave > 0) {
+            rb2[((wave - 1) * 4 + 0) * 64 + lane] = accG;
+            rb2[((wave - 1) * 4 + 1) * 64 + lane] = accU;
+            rb2[((wave - 1) * 4 + 2) * 64 + lane] = corG;
+            rb2[((wave - 1) * 4 + 3) * 64 + lane] = corU;
         }
-    }
-    if (n == 0 && gs < 2) {
-        float* sp = spart + (((int64_t)a * nbFp + bF) * 2 + (rt & 1)) * 16;
+        __syncthreads();
+        if (wave == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 4 * gs + i;
-            if (t < T) {
-                sp[t] = shi[i];
-                sp[8 + t] = slo[i];
+            for (int w = 0; w < 3; ++w) {
+                accG += rb2[(w * 4 + 0) * 64 + lane];
+                accU += rb2[(w * 4 + 1) * 64 + lane];
+                corG += rb2[(w * 4 + 2) * 64 + lane];
+                corU += rb2[(w * 4 + 3) * 64 + lane];
+            }
+            // lane holds (token t = 4*gs + i, row f = 16*rt + n); tokens < 8 live in gs 0..1.
+            // v = w * silu(g) * u becomes the down projection's A operand: rows m = t
+            // (bf16 hi) and 8 + t (bf16 lo), k = f, in the layout of one MFMA fragment
+            // per 32-wide block of F, plus the per-half-block row sums of both halves.
+            const int nbFp = g.dn.nch * 4;
+            const int bF = rt >> 1, kf = 16 * (rt & 1) + n;
+            uint16_t* af16 = reinterpret_cast<uint16_t*>(afrag) + ((int64_t)a * nbFp + bF) * 64 * 8;
+            float shi[4], slo[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * gs + i;
+                const float gv = accG[i] - QF<FMT>::kBias * corG[i];
+                const float uv = accU[i] - QF<FMT>::kBias * corU[i];
+                const float h = gv / (1.0f + expf(-gv)) * uv;
+                const float v = (t < T ? s_wt[a * kMaxDecodeT + t] : 0.f) * h;
+                const uint32_t hi = f2bf(v);
+                const uint32_t lo = f2bf(v - bf2f(hi));
+                shi[i] = bf2f(hi);
+                slo[i] = bf2f(lo);
+                if (t < T) {
+                    af16[(t + 16 * (kf >> 3)) * 8 + (kf & 7)] = (uint16_t)hi;
+                    af16[(8 + t + 16 * (kf >> 3)) * 8 + (kf & 7)] = (uint16_t)lo;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) {
+                    shi[i] += __shfl_xor(shi[i], off);
+                    slo[i] += __shfl_xor(slo[i], off);
+                }
+            }
+            if (n == 0 && gs < 2) {
+                float* sp = spart + (((int64_t)a * nbFp + bF) * 2 + (rt & 1)) * 16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 4 * gs + i;
+                    if (t < T) {
+                        sp[t] = shi[i];
+                        sp[8 + t] = slo[i];
+                    }
+                }
             }
         }
     }
+}
+
+template <int FMT, int NC>
+hipError_t launch_gateup_nc(const uint16_t* x, int T, const uint8_t* slots, const Geom& g, RouteBufs rb,
+                            DecodeBufs db, int max_items, hipStream_t st) {
+    static int granted = 64 * 1024;
+    static int per_cu[2 * kMaxDecodeT + 1] = {0};  // resident workgroups per CU, by T
+    const int lds = ((T * (g.H + 8) * 2 + 15) / 16) * 16 + 2 * 3 * 4 * 64 * 16;
+    hipError_t e = ensure_lds(k_gateup_decode<FMT, NC>, lds, granted);
+    if (e != hipSuccess) return e;
+    if (per_cu[T] == 0) {
+        int nb = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_gateup_decode<FMT, NC>, 256, lds);
+        if (e != hipSuccess) return e;
+        per_cu[T] = nb > 0 ? nb : 1;
+    }
+    int dev = 0, cus = 0;
+    hipGetDevice(&dev);
+    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int grid = per_cu[T] * cus;
+    if (grid > max_items) grid = max_items;
+    hipLaunchKernelGGL((k_gateup_decode<FMT, NC>), dim3(grid), dim3(256), lds, st, x, T, slots, g, rb.sx, rb.nact,
+                       rb.act, rb.wtab, db.afrag, db.spart);
+    return hipGetLastError();
 }
 
 hipError_t launch_gateup_decode(const uint16_t* x, int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb,
                                 DecodeBufs db, hipStream_t st) {
     const int maxA = (g.E < T * g.k ? g.E : T * g.k) + g.S;
-    dim3 grid(g.F / 16, maxA);
-    if (g.fmt == 1)
-        hipLaunchKernelGGL(k_gateup_decode<1>, grid, dim3(256), 0, st, x, T, layer_slots, g, rb.sx, rb.nact, rb.act,
-                           rb.wtab, db.afrag, db.spart);
-    else
-        hipLaunchKernelGGL(k_gateup_decode<2>, grid, dim3(256), 0, st, x, T, layer_slots, g, rb.sx, rb.nact, rb.act,
-                           rb.wtab, db.afrag, db.spart);
-    return hipGetLastError();
+    const int max_items = maxA * (g.F / 16);
+    const int per_wave = (g.gu.nch + 3) / 4;
+    if (g.fmt == 1) {
+        if (per_wave <= 2) return launch_gateup_nc<1, 2>(x, T, layer_slots, g, rb, db, max_items, st);
+        if (per_wave <= 4) return launch_gateup_nc<1, 4>(x, T, layer_slots, g, rb, db, max_items, st);
+        if (per_wave <= 6) return launch_gateup_nc<1, 6>(x, T, layer_slots, g, rb, db, max_items, st);
+        return launch_gateup_nc<1, 8>(x, T, layer_slots, g, rb, db, max_items, st);
+    }
+    if (per_wave <= 2) return launch_gateup_nc<2, 2>(x, T, layer_slots, g, rb, db, max_items, st);
+    if (per_wave <= 4) return launch_gateup_nc<2, 4>(x, T, layer_slots, g, rb, db, max_items, st);
+    if (per_wave <= 6) return launch_gateup_nc<2, 6>(x, T, layer_slots, g, rb, db, max_items, st);
+    return launch_gateup_nc<2, 8>(x, T, layer_slots, g, rb, db, max_items, st);
 }
 
-// ---------------------------------------------------------------- down + combine
-// Grid H/16, 512 threads.  Workgroup rt owns rows 16rt..16rt+15 of y; wave w
-// takes active experts a = w, w+8, ...; partial sums are added in wave order,
-// so the result does not depend on timing.  A = [w*h hi rows 0..7 | lo rows 8..15].
-template <int FMT>
-__global__ __launch_bounds__(512) void k_down_decode(const uint16_t* __restrict__ x, int T,
-                                                     const uint8_t* __restrict__ slots, Geom g,
+// ---------------------------------------------------------------- down projection
+constexpr int kRing = 4;  // chunks in flight per wave beyond the one being multiplied
+
+// Grid (ceil(H/128), maxA), 512 threads.  Workgroup (rg, a) computes the down
+// projection of active expert a for rows 128rg..128rg+127 (wave w: row tile
+// 8rg+w).  Each wave issues every weight load of its row tile (at most NC
+// chunks per pass), then the workgroup copies the expert's A fragments
+// (v hi rows 0..7 | v lo rows 8..15) into LDS; one wait, then the MFMAs.
+// Output: part[a][t][row].
+template <int FMT, int NC>
+__global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* __restrict__ slots, Geom g,
                                                      const int32_t* __restrict__ nact, const int32_t* __restrict__ act,
                                                      const uint32_t* __restrict__ afrag,
-                                                     const float* __restrict__ spart, uint16_t* __restrict__ y,
-                                                     int residual) {
-    __shared__ f32x4_t red[8][32];
-    const int rt = blockIdx.x;
+                                                     const float* __restrict__ spart, float* __restrict__ part) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int a = blockIdx.y;
+    if (a >= nact[0]) return;
+    const int rg = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, gs = lane >> 4, m = lane & 15;
-    const int nA = nact[0];
     const MatGeom& md = g.dn;
-    const int nbFp = md.nch * 4;
+    const int nbp = md.nch * 4;
+    const int rt = rg * 8 + wave;
+    const bool live = rt < g.H / 16;
+    const int e = act[a];
+    const uint8_t* Dt = slots + (int64_t)e * g.slot_bytes + g.d_off + (int64_t)(live ? rt : 0) * md.tile_bytes;
+    constexpr int CWN = FMT == 1 ? 4 : 2;
+    u32x4_t* frag = reinterpret_cast<u32x4_t*>(smem);
     const bool mrow = (m & 7) < T;
+    const float* sp = spart + (int64_t)a * nbp * 32;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, corr = acc;
-    for (int a = wave; a < nA; a += 8) {
-        const int e = act[a];
-        const uint8_t* Dt = slots + (int64_t)e * g.slot_bytes + g.d_off + (int64_t)rt * md.tile_bytes;
-        const u32x4_t* af = reinterpret_cast<const u32x4_t*>(afrag) + (int64_t)a * nbFp * 64;
-        const float* sp = spart + (int64_t)a * nbFp * 32;
-        for (int c = 0; c < md.nch; ++c) {
-            uint32_t cw[4];
-            load_codes<FMT>(Dt + (int64_t)c * md.chunk_bytes, lane, cw);
-            const u32x2_t sc = load_scales(Dt + (int64_t)c * md.chunk_bytes, QF<FMT>::kCW, n);
-            u32x4_t A[4];
+    constexpr int R = NC < kRing ? NC : kRing;
+    uint32_t cw[R][CWN];
+    u32x2_t sc[R];
+    float s0[R], s1[R];
+    // ring of kRing chunks with unconditional (clamped) loads, fully unrolled over NC
+    auto load = [&](int c, int i) {
+        c = min(c, md.nch - 1);
+        const int64_t off = (int64_t)c * md.chunk_bytes;
+        load_codes<FMT>(Dt + off, lane, cw[i]);
+        sc[i] = load_scales(Dt + off, QF<FMT>::kCW, n);
+        const int bq = c * 4 + gs;
+        s0[i] = sp[bq * 32 + m];
+        s1[i] = sp[bq * 32 + 16 + m];
+    };
+    auto compute = [&](int c, int i) {
+        u32x4_t A[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int b = c * 4 + j;
-                A[j] = (mrow && b < md.nb) ? af[(int64_t)b * 64 + lane] : u32x4_t{0u, 0u, 0u, 0u};
+        for (int j = 0; j < 4; ++j) {
+            const int b = c * 4 + j;
+            A[j] = (mrow && b < md.nb) ? frag[b * 64 + lane] : u32x4_t{0u, 0u, 0u, 0u};
+        }
+        const int bq = c * 4 + gs;
+        const float s = (mrow && bq < md.nb) ? s0[i] + s1[i] : 0.f;
+        chunk_mac<FMT>(cw[i], sc[i], A, s, gs, acc, corr);
+    };
+    for (int cb = 0; cb < md.nch; cb += NC) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) load(cb + i, i);
+        if (cb == 0) {
+            stage_lds(frag, reinterpret_cast<const u32x4_t*>(afrag) + (int64_t)a * nbp * 64, nbp * 64,
+                      [](int q) { return q; });
+            __syncthreads();
+        }
+        if (live) {
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+                if (cb + i < md.nch) compute(cb + i, i % R);
+                if (i + R < NC) load(cb + i + R, i % R);
             }
-            const int bq = c * 4 + gs;
-            const float s = (mrow && bq < md.nb) ? sp[bq * 32 + m] + sp[bq * 32 + 16 + m] : 0.f;
-            chunk_mac<FMT>(cw, sc, A, s, gs, acc, corr);
         }
     }
+    if (!live) return;
     f32x4_t v;
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = acc[i] - QF<FMT>::kBias * corr[i];
     f32x4_t other;
 #pragma unroll
     for (int i = 0; i < 4; ++i) other[i] = __shfl_xor(v[i], 32);
-    if (lane < 32) red[wave][lane] = v + other;
-    __syncthreads();
-    if (wave != 0 || lane >= 32) return;
-    f32x4_t s = red[0][lane];
-    for (int w = 1; w < 8; ++w) s += red[w][lane];
-    const int hrow = rt * 16 + n;
+    if (lane < 32) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = 4 * gs + i;
-        if (t < T) {
-            float out = s[i];
-            if (residual) out += bf2f(x[(int64_t)t * g.H + hrow]);
-            y[(int64_t)t * g.H + hrow] = (uint16_t)f2bf(out);
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * gs + i;
+            if (t < T) part[((int64_t)a * kMaxDecodeT + t) * g.H + rt * 16 + n] = v[i] + other[i];
         }
     }
 }
 
-hipError_t launch_down_decode(const uint16_t* x, int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb,
-                              DecodeBufs db, uint16_t* y, int residual, hipStream_t st) {
-    dim3 grid(g.H / 16);
-    if (g.fmt == 1)
-        hipLaunchKernelGGL(k_down_decode<1>, grid, dim3(512), 0, st, x, T, layer_slots, g, rb.nact, rb.act, db.afrag,
-                           db.spart, y, residual);
-    else
-        hipLaunchKernelGGL(k_down_decode<2>, grid, dim3(512), 0, st, x, T, layer_slots, g, rb.nact, rb.act, db.afrag,
-                           db.spart, y, residual);
+template <int FMT, int NC>
+hipError_t launch_down_nc(int T, const uint8_t* slots, const Geom& g, RouteBufs rb, DecodeBufs db, dim3 grid, int lds,
+                          hipStream_t st) {
+    static int granted = 64 * 1024;
+    hipError_t e = ensure_lds(k_down_decode<FMT, NC>, lds, granted);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_down_decode<FMT, NC>), grid, dim3(512), lds, st, T, slots, g, rb.nact, rb.act, db.afrag,
+                       db.spart, db.part);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_decode(int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb, DecodeBufs db,
+                              hipStream_t st) {
+    const int maxA = (g.E < T * g.k ? g.E : T * g.k) + g.S;
+    const int lds = g.dn.nch * 4 * 64 * 16;
+    dim3 grid((g.H + kDownRowsPerWG - 1) / kDownRowsPerWG, maxA);
+    const int nch = g.dn.nch;
+    if (g.fmt == 1) {
+        if (nch <= 4) return launch_down_nc<1, 4>(T, layer_slots, g, rb, db, grid, lds, st);
+        if (nch <= 8) return launch_down_nc<1, 8>(T, layer_slots, g, rb, db, grid, lds, st);
+        return launch_down_nc<1, 16>(T, layer_slots, g, rb, db, grid, lds, st);
+    }
+    if (nch <= 4) return launch_down_nc<2, 4>(T, layer_slots, g, rb, db, grid, lds, st);
+    if (nch <= 8) return launch_down_nc<2, 8>(T, layer_slots, g, rb, db, grid, lds, st);
+    return launch_down_nc<2, 16>(T, layer_slots, g, rb, db, grid, lds, st);
+}
+
+// ---------------------------------------------------------------- combine
+// y[t][h] = bf16( sum_{a < nact} part[a][t][h]  (+ x[t][h]) ), experts added in
+// ascending active order (routed experts by id, then the shared expert).
+__global__ __launch_bounds__(256) void k_combine_decode(const uint16_t* __restrict__ x, int T, int H,
+                                                        const int32_t* __restrict__ nact,
+                                                        const float* __restrict__ part, uint16_t* __restrict__ y,
+                                                        int residual) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= T * H) return;
+    const int nA = nact[0];
+    const float* p = part + i;  // part[a][t][h] with t*H + h = i
+    const int64_t stride = (int64_t)kMaxDecodeT * H;
+    float s = 0.f;
+    int a = 0;
+    for (; a + 4 <= nA; a += 4) {
+        const float p0 = p[(a + 0) * stride], p1 = p[(a + 1) * stride];
+        const float p2 = p[(a + 2) * stride], p3 = p[(a + 3) * stride];
+        s += p0;
+        s += p1;
+        s += p2;
+        s += p3;
+    }
+    for (; a < nA; ++a) s += p[a * stride];
+    if (residual) s += bf2f(x[i]);
+    y[i] = (uint16_t)f2bf(s);
+}
+
+hipError_t launch_combine_decode(const uint16_t* x, int T, const Geom& g, RouteBufs rb, DecodeBufs db, uint16_t* y,
+                                 int residual, hipStream_t st) {
+    hipLaunchKernelGGL(k_combine_decode, dim3((T * g.H + 255) / 256), dim3(256), 0, st, x, T, g.H, rb.nact, db.part, y,
+                       residual);
     return hipGetLastError();
 }
 

@@ -169,12 +169,13 @@ def test_zero_tokens_and_error_paths(torch_cuda):
 def test_create_rejects_bad_geometry(torch_cuda):
     from quantized_expert_ffn_softmax_amd import MOE_EINVAL, MOE_ENOMEM, MOE_Q4B32 as Q4, MoEContext, MoEError
     for args in [(100, 64, 8, 0, 2, 1, Q4, 4), (128, 64, 8, 0, 9, 1, Q4, 4), (128, 64, 8, 2, 2, 1, Q4, 4),
-                 (128, 64, 8, 0, 2, 1, 7, 4), (128, 64, 8, 0, 2, 1, Q4, 0)]:
+                 (128, 64, 8, 0, 2, 1, 7, 4), (128, 64, 8, 0, 2, 1, Q4, 0), (8192, 64, 8, 0, 2, 1, Q4, 4),
+                 (4096, 4096, 8, 0, 2, 1, Q4, 4)]:
         with pytest.raises(MoEError) as ei:
             MoEContext(*args)
         assert ei.value.status == MOE_EINVAL
     # an arena far beyond the device: ENOMEM, and nothing leaks across repeated attempts
     for _ in range(3):
         with pytest.raises(MoEError) as ei:
-            MoEContext(8192, 8192, 1024, 1, 8, 64, Q4, 4)
+            MoEContext(4096, 2048, 1024, 1, 8, 64, Q4, 4)  # 64 x 1025 experts x 14.2 MB
         assert ei.value.status == MOE_ENOMEM
