@@ -136,7 +136,8 @@ def main():
     total_bytes = sum(step_bytes(i) for i in range(args.steps))
     hbm_gbps = total_bytes / (ms_total / 1e3) / 1e9
 
-    # ---- profiled pass: HIP events around every kernel, on the launch stream
+    # ---- profiled pass: a HIP event pair bound to each kernel dispatch (hipExtLaunchKernelGGL), on the
+    #      stream the kernels run on
     nprof = min(args.steps, 4 * n_pairs if not chain else len(xs))
     ctx.profile_read()
     for i in range(nprof):

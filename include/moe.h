@@ -105,7 +105,7 @@ typedef struct {
 } moe_layer_weights;
 
 #define MOE_FWD_RESIDUAL 1 /* x_{l+1} = bf16(fp32(x_l) + y_l); else x_{l+1} = bf16(y_l) */
-#define MOE_FWD_PROFILE 2  /* record a HIP event pair around every kernel (read with moe_profile_read) */
+#define MOE_FWD_PROFILE 2  /* time every kernel with a HIP event pair bound to its dispatch (moe_profile_read) */
 
 /* One forward pass through layers [layer_begin, layer_begin + layer_count).
  *   x      : [T x H] bf16, device, input of the first layer
@@ -178,7 +178,7 @@ typedef enum {
 typedef struct {
     int32_t kernel; /* moe_kernel_kind */
     int32_t layer;
-    float ms;       /* hipEventElapsedTime between the events around the launch */
+    float ms;       /* hipEventElapsedTime of the start/stop events bound to the kernel's dispatch */
 } moe_kernel_time;
 
 /* Durations of the kernels launched by moe_forward calls made with

@@ -306,10 +306,12 @@ namespace {
 
 constexpr size_t kMaxProfiled = 65536;
 
-// Runs launch() between two recorded events when profiling is on.
+// Runs launch(Launch) on st; when profiling, with a start/stop event pair bound
+// to the dispatch (the events time the kernel itself).
 extern "C++" template <class F>
 moe_status timed(moe_ctx* c, bool prof, int kind, int layer, hipStream_t st, F launch, const char* what) {
-    size_t i = c->prof_recs.size();
+    Launch lc{st};
+    const size_t i = c->prof_recs.size();
     prof = prof && i < kMaxProfiled;
     if (prof) {
         while (c->prof_events.size() < 2 * (i + 1)) {
@@ -317,14 +319,12 @@ moe_status timed(moe_ctx* c, bool prof, int kind, int layer, hipStream_t st, F l
             HIP_TRY(c, hipEventCreate(&e));
             c->prof_events.push_back(e);
         }
-        HIP_TRY(c, hipEventRecord(c->prof_events[2 * i], st));
+        lc.start = c->prof_events[2 * i];
+        lc.stop = c->prof_events[2 * i + 1];
     }
-    hipError_t e = launch();
+    hipError_t e = launch(lc);
     if (e != hipSuccess) return hip_fail(c, e, what);
-    if (prof) {
-        HIP_TRY(c, hipEventRecord(c->prof_events[2 * i + 1], st));
-        c->prof_recs.push_back(moe_kernel_time{kind, layer, 0.f});
-    }
+    if (prof) c->prof_recs.push_back(moe_kernel_time{kind, layer, 0.f});
     return MOE_OK;
 }
 
@@ -342,13 +342,14 @@ moe_status check_layer_ready(moe_ctx* c, int layer, bool need_experts) {
 moe_status route_decode(moe_ctx* c, int layer, const uint16_t* x, int T, int32_t* trace_ids, float* trace_w,
                         hipStream_t st, bool prof = false) {
     const Geom& g = c->g;
-    moe_status s = timed(c, prof, MOE_K_ROUTER, layer, st, [&] {
+    moe_status s = timed(c, prof, MOE_K_ROUTER, layer, st, [&](const Launch& lc) {
         return launch_router_decode(x, T, c->routers + (size_t)layer * g.E * g.H, c->biases + (size_t)layer * g.E, g,
-                                    c->rb, st);
+                                    c->rb, lc);
     }, "router kernel launch");
     if (s != MOE_OK) return s;
     return timed(c, prof, MOE_K_TOPK_SORT, layer, st,
-                 [&] { return launch_topk_sort_decode(T, g, c->rb, trace_ids, trace_w, st); }, "top-k kernel launch");
+                 [&](const Launch& lc) { return launch_topk_sort_decode(T, g, c->rb, trace_ids, trace_w, lc); },
+                 "top-k kernel launch");
 }
 
 }  // namespace
@@ -415,14 +416,16 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
                                     a->trace_w ? a->trace_w + (size_t)i * T * g.k : nullptr, st, prof);
         if (s != MOE_OK) return s;
         const uint8_t* slots = c->arena + (size_t)l * ES * g.slot_bytes;
-        s = timed(c, prof, MOE_K_GATEUP, l, st, [&] { return launch_gateup_decode(xin, T, slots, g, c->rb, c->db, st); },
+        s = timed(c, prof, MOE_K_GATEUP, l, st,
+                  [&](const Launch& lc) { return launch_gateup_decode(xin, T, slots, g, c->rb, c->db, lc); },
                   "gate/up kernel launch");
         if (s != MOE_OK) return s;
-        s = timed(c, prof, MOE_K_DOWN, l, st, [&] { return launch_down_decode(T, slots, g, c->rb, c->db, st); },
+        s = timed(c, prof, MOE_K_DOWN, l, st,
+                  [&](const Launch& lc) { return launch_down_decode(T, slots, g, c->rb, c->db, lc); },
                   "down kernel launch");
         if (s != MOE_OK) return s;
-        s = timed(c, prof, MOE_K_COMBINE, l, st, [&] {
-            return launch_combine_decode(xin, T, g, c->rb, c->db, yout, a->flags & MOE_FWD_RESIDUAL, st);
+        s = timed(c, prof, MOE_K_COMBINE, l, st, [&](const Launch& lc) {
+            return launch_combine_decode(xin, T, g, c->rb, c->db, yout, a->flags & MOE_FWD_RESIDUAL, lc);
         }, "combine kernel launch");
         if (s != MOE_OK) return s;
         xin = yout;

@@ -105,17 +105,23 @@ struct DecodeBufs {
 
 constexpr int kDownRowsPerWG = 128;  // 8 waves x 16 rows
 
+// Stream and optional profiling events of one launch.
+struct Launch {
+    hipStream_t st;
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
 // Launchers (return hipGetLastError()).
 hipError_t launch_repack(const uint8_t* canon, uint8_t* slots, int count, const Geom& g, hipStream_t st);
 hipError_t launch_router_decode(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const Geom& g,
-                                RouteBufs rb, hipStream_t st);
+                                RouteBufs rb, const Launch& lc);
 hipError_t launch_topk_sort_decode(int T, const Geom& g, RouteBufs rb, int32_t* trace_ids, float* trace_w,
-                                   hipStream_t st);
+                                   const Launch& lc);
 hipError_t launch_gateup_decode(const uint16_t* x, int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb,
-                                DecodeBufs db, hipStream_t st);
+                                DecodeBufs db, const Launch& lc);
 hipError_t launch_down_decode(int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb, DecodeBufs db,
-                              hipStream_t st);
+                              const Launch& lc);
 hipError_t launch_combine_decode(const uint16_t* x, int T, const Geom& g, RouteBufs rb, DecodeBufs db, uint16_t* y,
-                                 int residual, hipStream_t st);
+                                 int residual, const Launch& lc);
 
 }  // namespace moe

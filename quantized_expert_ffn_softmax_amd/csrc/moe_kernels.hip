@@ -29,8 +29,19 @@
 #include <stdint.h>
 
 #include "moe_internal.h"
+#include <hip/hip_ext.h>
 
 namespace moe {
+
+// Launch on lc.st; with profiling events, the start/stop events are bound to the
+// dispatch itself (hipExtLaunchKernelGGL), so they time the kernel alone.
+template <class K, class... Args>
+inline void launch(K kernel, dim3 grid, dim3 block, uint32_t lds, const Launch& lc, Args... args) {
+    if (lc.start)
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, lc.st, lc.start, lc.stop, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, lc.st, args...);
+}
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -375,12 +386,12 @@ __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restric
 }
 
 hipError_t launch_router_decode(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const Geom& g,
-                                RouteBufs rb, hipStream_t st) {
+                                RouteBufs rb, const Launch& lc) {
     static int granted = 64 * 1024;
     const int lds = T * g.H * 2;
     hipError_t e = ensure_lds(k_router_decode, lds, granted);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_router_decode, dim3((g.E + 3) / 4), dim3(256), lds, st, x, T, Wr, bias, g.E, g.H,
+    launch(k_router_decode, dim3((g.E + 3) / 4), dim3(256), lds, lc, x, T, Wr, bias, g.E, g.H,
                        g.gu.nch * 4, rb.logits, rb.sx);
     return hipGetLastError();
 }
@@ -508,13 +519,13 @@ __global__ __launch_bounds__(256) void k_topk_sort(int T, int E, int k, int S, R
 }
 
 hipError_t launch_topk_sort_decode(int T, const Geom& g, RouteBufs rb, int32_t* trace_ids, float* trace_w,
-                                   hipStream_t st) {
+                                   const Launch& lc) {
     if (g.E <= 256)
-        hipLaunchKernelGGL(k_topk_sort<4>, dim3(1), dim3(256), 0, st, T, g.E, g.k, g.S, rb, trace_ids, trace_w);
+        launch(k_topk_sort<4>, dim3(1), dim3(256), 0, lc, T, g.E, g.k, g.S, rb, trace_ids, trace_w);
     else if (g.E <= 512)
-        hipLaunchKernelGGL(k_topk_sort<8>, dim3(1), dim3(256), 0, st, T, g.E, g.k, g.S, rb, trace_ids, trace_w);
+        launch(k_topk_sort<8>, dim3(1), dim3(256), 0, lc, T, g.E, g.k, g.S, rb, trace_ids, trace_w);
     else
-        hipLaunchKernelGGL(k_topk_sort<16>, dim3(1), dim3(256), 0, st, T, g.E, g.k, g.S, rb, trace_ids, trace_w);
+        launch(k_topk_sort<16>, dim3(1), dim3(256), 0, lc, T, g.E, g.k, g.S, rb, trace_ids, trace_w);
     return hipGetLastError();
 }
 
@@ -674,7 +685,7 @@ __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restric
 
 template <int FMT, int NC>
 hipError_t launch_gateup_nc(const uint16_t* x, int T, const uint8_t* slots, const Geom& g, RouteBufs rb,
-                            DecodeBufs db, int max_items, hipStream_t st) {
+                            DecodeBufs db, int max_items, const Launch& lc) {
     static int granted = 64 * 1024;
     static int per_cu[2 * kMaxDecodeT + 1] = {0};  // resident workgroups per CU, by T
     const int lds = ((T * (g.H + 8) * 2 + 15) / 16) * 16 + 2 * 3 * 4 * 64 * 16;
@@ -691,26 +702,26 @@ hipError_t launch_gateup_nc(const uint16_t* x, int T, const uint8_t* slots, cons
     hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     int grid = per_cu[T] * cus;
     if (grid > max_items) grid = max_items;
-    hipLaunchKernelGGL((k_gateup_decode<FMT, NC>), dim3(grid), dim3(256), lds, st, x, T, slots, g, rb.sx, rb.nact,
+    launch(k_gateup_decode<FMT, NC>, dim3(grid), dim3(256), lds, lc, x, T, slots, g, rb.sx, rb.nact,
                        rb.act, rb.wtab, db.afrag, db.spart);
     return hipGetLastError();
 }
 
 hipError_t launch_gateup_decode(const uint16_t* x, int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb,
-                                DecodeBufs db, hipStream_t st) {
+                                DecodeBufs db, const Launch& lc) {
     const int maxA = (g.E < T * g.k ? g.E : T * g.k) + g.S;
     const int max_items = maxA * (g.F / 16);
     const int per_wave = (g.gu.nch + 3) / 4;
     if (g.fmt == 1) {
-        if (per_wave <= 2) return launch_gateup_nc<1, 2>(x, T, layer_slots, g, rb, db, max_items, st);
-        if (per_wave <= 4) return launch_gateup_nc<1, 4>(x, T, layer_slots, g, rb, db, max_items, st);
-        if (per_wave <= 6) return launch_gateup_nc<1, 6>(x, T, layer_slots, g, rb, db, max_items, st);
-        return launch_gateup_nc<1, 8>(x, T, layer_slots, g, rb, db, max_items, st);
+        if (per_wave <= 2) return launch_gateup_nc<1, 2>(x, T, layer_slots, g, rb, db, max_items, lc);
+        if (per_wave <= 4) return launch_gateup_nc<1, 4>(x, T, layer_slots, g, rb, db, max_items, lc);
+        if (per_wave <= 6) return launch_gateup_nc<1, 6>(x, T, layer_slots, g, rb, db, max_items, lc);
+        return launch_gateup_nc<1, 8>(x, T, layer_slots, g, rb, db, max_items, lc);
     }
-    if (per_wave <= 2) return launch_gateup_nc<2, 2>(x, T, layer_slots, g, rb, db, max_items, st);
-    if (per_wave <= 4) return launch_gateup_nc<2, 4>(x, T, layer_slots, g, rb, db, max_items, st);
-    if (per_wave <= 6) return launch_gateup_nc<2, 6>(x, T, layer_slots, g, rb, db, max_items, st);
-    return launch_gateup_nc<2, 8>(x, T, layer_slots, g, rb, db, max_items, st);
+    if (per_wave <= 2) return launch_gateup_nc<2, 2>(x, T, layer_slots, g, rb, db, max_items, lc);
+    if (per_wave <= 4) return launch_gateup_nc<2, 4>(x, T, layer_slots, g, rb, db, max_items, lc);
+    if (per_wave <= 6) return launch_gateup_nc<2, 6>(x, T, layer_slots, g, rb, db, max_items, lc);
+    return launch_gateup_nc<2, 8>(x, T, layer_slots, g, rb, db, max_items, lc);
 }
 
 // ---------------------------------------------------------------- down projection
@@ -803,29 +814,29 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* __res
 
 template <int FMT, int NC>
 hipError_t launch_down_nc(int T, const uint8_t* slots, const Geom& g, RouteBufs rb, DecodeBufs db, dim3 grid, int lds,
-                          hipStream_t st) {
+                          const Launch& lc) {
     static int granted = 64 * 1024;
     hipError_t e = ensure_lds(k_down_decode<FMT, NC>, lds, granted);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_down_decode<FMT, NC>), grid, dim3(512), lds, st, T, slots, g, rb.nact, rb.act, db.afrag,
+    launch(k_down_decode<FMT, NC>, grid, dim3(512), lds, lc, T, slots, g, rb.nact, rb.act, db.afrag,
                        db.spart, db.part);
     return hipGetLastError();
 }
 
 hipError_t launch_down_decode(int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb, DecodeBufs db,
-                              hipStream_t st) {
+                              const Launch& lc) {
     const int maxA = (g.E < T * g.k ? g.E : T * g.k) + g.S;
     const int lds = g.dn.nch * 4 * 64 * 16;
     dim3 grid((g.H + kDownRowsPerWG - 1) / kDownRowsPerWG, maxA);
     const int nch = g.dn.nch;
     if (g.fmt == 1) {
-        if (nch <= 4) return launch_down_nc<1, 4>(T, layer_slots, g, rb, db, grid, lds, st);
-        if (nch <= 8) return launch_down_nc<1, 8>(T, layer_slots, g, rb, db, grid, lds, st);
-        return launch_down_nc<1, 16>(T, layer_slots, g, rb, db, grid, lds, st);
+        if (nch <= 4) return launch_down_nc<1, 4>(T, layer_slots, g, rb, db, grid, lds, lc);
+        if (nch <= 8) return launch_down_nc<1, 8>(T, layer_slots, g, rb, db, grid, lds, lc);
+        return launch_down_nc<1, 16>(T, layer_slots, g, rb, db, grid, lds, lc);
     }
-    if (nch <= 4) return launch_down_nc<2, 4>(T, layer_slots, g, rb, db, grid, lds, st);
-    if (nch <= 8) return launch_down_nc<2, 8>(T, layer_slots, g, rb, db, grid, lds, st);
-    return launch_down_nc<2, 16>(T, layer_slots, g, rb, db, grid, lds, st);
+    if (nch <= 4) return launch_down_nc<2, 4>(T, layer_slots, g, rb, db, grid, lds, lc);
+    if (nch <= 8) return launch_down_nc<2, 8>(T, layer_slots, g, rb, db, grid, lds, lc);
+    return launch_down_nc<2, 16>(T, layer_slots, g, rb, db, grid, lds, lc);
 }
 
 // ---------------------------------------------------------------- combine
@@ -856,8 +867,8 @@ __global__ __launch_bounds__(256) void k_combine_decode(const uint16_t* __restri
 }
 
 hipError_t launch_combine_decode(const uint16_t* x, int T, const Geom& g, RouteBufs rb, DecodeBufs db, uint16_t* y,
-                                 int residual, hipStream_t st) {
-    hipLaunchKernelGGL(k_combine_decode, dim3((T * g.H + 255) / 256), dim3(256), 0, st, x, T, g.H, rb.nact, db.part, y,
+                                 int residual, const Launch& lc) {
+    launch(k_combine_decode, dim3((T * g.H + 255) / 256), dim3(256), 0, lc, x, T, g.H, rb.nact, db.part, y,
                        residual);
     return hipGetLastError();
 }
