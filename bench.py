@@ -12,7 +12,10 @@ weights and the 256 MB Infinity Cache does not serve repeated reads.
 
 Other workloads (--workload): C3 (the 48-layer chain with residual adds at
 window 1/4/8) and C4 (the 43-layer DeepSeek-shaped chain, 256+1 experts,
-q4b32); a step is then one full chain pass.
+q4b32); a step is then one full chain pass.  C5 is the DeepSeek-shaped
+prefill chunk (4096 tokens x hidden 4096, 256+1 experts, top-6, FF 2048,
+q4b32, Zipf-skewed routing): a step is one moe_forward of the whole chunk,
+and the roofline is that of the gate/up grouped GEMM on bf16 MFMA.
 
 Printed: one JSON line with tokens/s, HBM GB/s on expert bytes, the roofline
 of the dominant kernel (gate/up, measured with HIP events recorded around
@@ -31,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s on expert weights (decode, window 4)"
 
 
@@ -43,7 +47,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=960)
     p.add_argument("--warmup", type=int, default=96)
-    p.add_argument("--workload", default="C2", choices=["C2", "C3", "C4"])
+    p.add_argument("--workload", default="C2", choices=["C2", "C3", "C4", "C5"])
     p.add_argument("--T", type=int, default=4, help="tokens per window")
     p.add_argument("--layers", type=int, default=0, help="resident layers (default: 48 for C2/C3, 43 for C4)")
     p.add_argument("--windows", type=int, default=16)
@@ -58,6 +62,8 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported (no collectives)"}))
         sys.exit(2)
+    if args.workload == "C5":
+        return run_prefill(args)
     import torch
 
     import moe_inputs as mi
@@ -210,6 +216,112 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, args, L, chain, T)
+    ctx.close()
+    print(json.dumps(result), flush=True)
+
+
+def run_prefill(args):
+    """C5: one 4096-token prefill chunk through one resident layer per step."""
+    import torch
+
+    import moe_inputs as mi
+    from moe_inputs.configs import C5
+    from quantized_expert_ffn_softmax_amd import MoEContext
+
+    cfg = C5
+    T = cfg.T[0]
+    steps = args.steps if args.steps != 960 else 20
+    warmup = args.warmup if args.warmup != 96 else 3
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload C5: T={T} H={cfg.H} F={cfg.F} E={cfg.E}+{cfg.S} k={cfg.k}")
+    ctx = MoEContext(cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, 1, cfg.fmt, T)
+    W, b, ex = mi.layer_inputs(cfg, args.seed, 0)
+    ctx.load(0, router_w=W, router_bias=b, experts=ex)
+    del ex
+    x = torch.from_numpy(mi.gen_x(args.seed, 0, T, cfg.H).view(np.int16)).view(torch.bfloat16).to(dev)
+    y = torch.empty_like(x)
+    log("[bench] loaded")
+    for _ in range(warmup):
+        ctx.forward(x, y=y)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        ctx.forward(x, y=y)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / steps
+    log(f"[bench] timed {steps} steps: {ms_per_step:.3f} ms/step")
+    # profiled pass: HIP event pairs bound to each dispatch, on the launch stream
+    ctx.profile_read()
+    for _ in range(steps):
+        ctx.forward(x, y=y, profile=True)
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for name, _, ms in ctx.profile_read():
+        per_kernel.setdefault(name, []).append(ms)
+    n_sort = 3  # histogram, scan, scatter launches per step
+    kernels_us = {k: round(1e3 * float(np.mean(v)) * (n_sort if k == "pf_sort" else 1), 2)
+                  for k, v in per_kernel.items()}
+    log(f"[bench] per-kernel mean us (events): {kernels_us}")
+    rows = T * cfg.k + cfg.S * T
+    gemm1_flops = 2.0 * rows * cfg.H * 2 * cfg.F
+    gemm2_flops = 2.0 * rows * cfg.F * cfg.H
+    g1_s = float(np.mean(per_kernel["pf_gemm1"])) / 1e3
+    g2_s = float(np.mean(per_kernel["pf_gemm2"])) / 1e3
+    g1_tflops = gemm1_flops / g1_s / 1e12
+    g2_tflops = gemm2_flops / g2_s / 1e12
+    layer_tflops = (gemm1_flops + gemm2_flops + 2.0 * T * cfg.E * cfg.H) / (ms_per_step / 1e3) / 1e12
+    weight_bytes = (cfg.E + cfg.S) * cfg.expert_bytes
+    log(f"[bench] gemm1 {g1_tflops:.0f} TFLOP/s, gemm2 {g2_tflops:.0f} TFLOP/s, layer {layer_tflops:.0f} TFLOP/s")
+    result = {
+        "metric": "MoE-layer tokens/s (prefill chunk) + MFMA TFLOP/s of the grouped GEMMs",
+        "value": round(T * steps / (ms_total / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "C5: one DeepSeek-shaped 4096-token prefill chunk through one layer per step",
+                   "T": T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "S": cfg.S, "k": cfg.k, "quant": "q4b32",
+                   "zipf_s": cfg.bias_param, "seed": args.seed},
+        "layer_TFLOPs": round(layer_tflops, 1),
+        "weight_GBps": round(weight_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        "kernels_us": kernels_us,
+        "gemm2_TFLOPs": round(g2_tflops, 1),
+        "roofline": {
+            "kernel": "k_pf_gemm<q4,gate/up>",
+            "bound": "mfma",
+            "achieved": round(g1_tflops, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(g1_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(g1_s * 1e6, 2),
+            "flops_per_launch": gemm1_flops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        W, b, ex = mi.layer_inputs(cfg, args.seed, 0)
+        xs = mi.gen_x(args.seed, 0, T, cfg.H)
+        n = 0
+        t1 = time.perf_counter()
+        while time.perf_counter() - t1 < args.cpu_seconds and n < T:
+            oracle.moe_layer(np.ascontiguousarray(xs[n:n + 8]), cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, cfg.fmt, W, b, ex,
+                             cfg.expert_bytes)
+            n += 8
+        dt = time.perf_counter() - t1
+        result["cpu_baseline"] = {"value": round(n / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+                                  "kind": "oracle", "sample": f"first {n} tokens of the chunk, 8 per oracle call",
+                                  "seconds": round(dt, 2)}
     ctx.close()
     print(json.dumps(result), flush=True)
 

@@ -151,7 +151,14 @@ moe_status moe_route(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, int3
 
 /* Whole layers (steps 1-5) for T tokens; see moe_fwd_args.  MOE_ESTATE if a
  * layer's router or any of its experts is not loaded, MOE_ERANGE if
- * T > max_tokens, MOE_OK and no work for T = 0. */
+ * T > max_tokens, MOE_OK and no work for T = 0.
+ * T <= 8 (a decode or verify window) runs the GEMV-shaped decode kernels,
+ * whose expert arithmetic is exact up to fp32 accumulation.  T > 8 (prefill,
+ * "Qwen3.8-Flash-Next UD-Q4_K_XL 引擎对比", section 四: compute-bound) groups
+ * the tokens by expert and runs grouped GEMMs on bf16 MFMA; there the
+ * dequantised weights and the SwiGLU activations are rounded to bf16 before
+ * the contractions.  Routing (ids, weights, offsets, perm) is exact on both
+ * paths. */
 moe_status moe_forward(moe_ctx* ctx, const moe_fwd_args* args, void* hip_stream);
 
 /* Wait for the context's work, free everything it owns.  NULL is a no-op. */
@@ -169,7 +176,7 @@ typedef enum {
     MOE_K_COMBINE = 4,      /* ordered weighted combine (+ residual), decode path */
     MOE_K_PF_ROUTER = 5,    /* prefill router */
     MOE_K_PF_TOPK = 6,      /* prefill top-k + weights */
-    MOE_K_PF_SORT = 7,      /* prefill counting sort */
+    MOE_K_PF_SORT = 7,      /* prefill counting sort (three launches: histogram, scan, scatter) */
     MOE_K_PF_GEMM1 = 8,     /* prefill grouped GEMM gate/up + SwiGLU */
     MOE_K_PF_GEMM2 = 9,     /* prefill grouped GEMM down */
     MOE_K_PF_COMBINE = 10   /* prefill weighted combine */

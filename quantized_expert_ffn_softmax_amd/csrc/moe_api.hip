@@ -59,6 +59,9 @@ struct moe_ctx {
     size_t scratch_bytes = 0;
     RouteBufs rb{};
     DecodeBufs db{};
+    PrefillBufs pb{};
+    bool prefill = false;          // max_tokens > kMaxDecodeT: prefill scratch present
+    float* rstat = nullptr;        // L x 2: max router row norm, max |bias| (prefill candidate bound)
     uint16_t* xbuf[2] = {nullptr, nullptr};
     int maxA = 0;
     int decode_T = 0;
@@ -97,6 +100,7 @@ void free_ctx(moe_ctx* c) {
     }
     if (c->load_stream) hipStreamDestroy(c->load_stream);
     if (c->scratch) hipFree(c->scratch);
+    if (c->rstat) hipFree(c->rstat);
     if (c->biases) hipFree(c->biases);
     if (c->routers) hipFree(c->routers);
     if (c->arena) hipFree(c->arena);
@@ -162,29 +166,12 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     if (e != hipSuccess) { free_ctx(c); return fail(MOE_EHIP, "hipSetDevice: %s", hipGetErrorString(e)); }
     const int L = cfg->n_layers, ES = cfg->n_experts + cfg->n_shared;
     c->arena_bytes = (uint64_t)L * ES * g.slot_bytes;
-    size_t free_b = 0, total_b = 0;
-    hipMemGetInfo(&free_b, &total_b);
-    if (c->arena_bytes + (64ull << 20) > free_b) {
-        free_ctx(c);
-        return fail(MOE_ENOMEM, "expert arena of %llu bytes does not fit in %llu free bytes",
-                    (unsigned long long)((uint64_t)L * ES * g.slot_bytes), (unsigned long long)free_b);
-    }
-    if (hipMalloc(&c->arena, c->arena_bytes) != hipSuccess) {
-        hipGetLastError();
-        free_ctx(c);
-        return fail(MOE_ENOMEM, "hipMalloc of the %llu-byte expert arena failed", (unsigned long long)c->arena_bytes);
-    }
-    if (hipMalloc(&c->routers, (size_t)L * g.E * g.H * 2) != hipSuccess ||
-        hipMalloc(&c->biases, (size_t)L * g.E * 4) != hipSuccess) {
-        hipGetLastError();
-        free_ctx(c);
-        return fail(MOE_ENOMEM, "router allocation failed");
-    }
-    // scratch for the decode path (T <= 8)
+    // scratch layout: decode buffers (T <= 8), then prefill buffers when max_tokens > 8
     const int Td = std::min(cfg->max_tokens, kMaxDecodeT);
     c->decode_T = Td;
     c->maxA = std::min(g.E, kMaxDecodeT * g.k) + g.S;
     const int nbHp = g.gu.nch * 4, nbFp = g.dn.nch * 4;
+    const int Tm = std::max(cfg->max_tokens, kMaxDecodeT);
     Carver cv;
     const size_t o_logits = cv.take<double>((size_t)kMaxDecodeT * g.E);
     const size_t o_sx = cv.take<float>((size_t)nbHp * 16);
@@ -199,9 +186,51 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     const size_t o_afrag = cv.take<uint32_t>((size_t)c->maxA * nbFp * 64 * 4);
     const size_t o_spart = cv.take<float>((size_t)c->maxA * nbFp * 32);
     const size_t o_part = cv.take<float>((size_t)c->maxA * kMaxDecodeT * g.H);
-    const size_t o_x0 = cv.take<uint16_t>((size_t)kMaxDecodeT * g.H);
-    const size_t o_x1 = cv.take<uint16_t>((size_t)kMaxDecodeT * g.H);
+    const size_t o_x0 = cv.take<uint16_t>((size_t)Tm * g.H);
+    const size_t o_x1 = cv.take<uint16_t>((size_t)Tm * g.H);
+    c->prefill = cfg->max_tokens > kMaxDecodeT;
+    size_t p_logits = 0, p_ids = 0, p_w = 0, p_blkcnt = 0, p_rank = 0, p_off = 0, p_perm = 0, p_inv = 0, p_rowtok = 0,
+           p_blkbase = 0, p_tiles = 0, p_ntiles = 0, p_h = 0, p_o = 0;
+    if (c->prefill) {
+        const size_t P = (size_t)Tm * g.k, rows = P + (size_t)g.S * Tm;
+        const size_t nblk = (size_t)(Tm + kPfBlockTokens - 1) / kPfBlockTokens;
+        c->pb.max_tiles = prefill_max_tiles(Tm, g.k, g.E, g.S);
+        p_logits = cv.take<float>((size_t)Tm * g.E);
+        p_ids = cv.take<int32_t>(P);
+        p_w = cv.take<float>(P);
+        p_blkcnt = cv.take<uint32_t>(nblk * g.E);
+        p_rank = cv.take<int32_t>(P);
+        p_off = cv.take<int32_t>((size_t)g.E + 1);
+        p_perm = cv.take<int32_t>(P);
+        p_inv = cv.take<int32_t>(P);
+        p_rowtok = cv.take<int32_t>(rows);
+        p_blkbase = cv.take<int32_t>(nblk * g.E);
+        p_tiles = cv.take<int32_t>((size_t)c->pb.max_tiles * 4);
+        p_ntiles = cv.take<int32_t>(1);
+        p_h = cv.take<uint16_t>(rows * g.F);
+        p_o = cv.take<float>(rows * g.H);
+    }
     c->scratch_bytes = cv.off;
+    size_t free_b = 0, total_b = 0;
+    hipMemGetInfo(&free_b, &total_b);
+    if (c->arena_bytes + c->scratch_bytes + (64ull << 20) > free_b) {
+        free_ctx(c);
+        return fail(MOE_ENOMEM, "expert arena (%llu bytes) and scratch (%llu bytes) do not fit in %llu free bytes",
+                    (unsigned long long)c->arena_bytes, (unsigned long long)c->scratch_bytes,
+                    (unsigned long long)free_b);
+    }
+    if (hipMalloc(&c->arena, c->arena_bytes) != hipSuccess) {
+        hipGetLastError();
+        free_ctx(c);
+        return fail(MOE_ENOMEM, "hipMalloc of the %llu-byte expert arena failed", (unsigned long long)c->arena_bytes);
+    }
+    if (hipMalloc(&c->routers, (size_t)L * g.E * g.H * 2) != hipSuccess ||
+        hipMalloc(&c->biases, (size_t)L * g.E * 4) != hipSuccess ||
+        hipMalloc(&c->rstat, (size_t)L * 2 * 4) != hipSuccess) {
+        hipGetLastError();
+        free_ctx(c);
+        return fail(MOE_ENOMEM, "router allocation failed");
+    }
     if (hipMalloc(&c->scratch, c->scratch_bytes) != hipSuccess) {
         hipGetLastError();
         free_ctx(c);
@@ -223,8 +252,25 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     c->db.part = (float*)(b + o_part);
     c->xbuf[0] = (uint16_t*)(b + o_x0);
     c->xbuf[1] = (uint16_t*)(b + o_x1);
+    if (c->prefill) {
+        c->pb.logits = (float*)(b + p_logits);
+        c->pb.ids = (int32_t*)(b + p_ids);
+        c->pb.w = (float*)(b + p_w);
+        c->pb.blkcnt = (uint32_t*)(b + p_blkcnt);
+        c->pb.rank = (int32_t*)(b + p_rank);
+        c->pb.offsets = (int32_t*)(b + p_off);
+        c->pb.perm = (int32_t*)(b + p_perm);
+        c->pb.inv = (int32_t*)(b + p_inv);
+        c->pb.rowtok = (int32_t*)(b + p_rowtok);
+        c->pb.blkbase = (int32_t*)(b + p_blkbase);
+        c->pb.tiles = (int32_t*)(b + p_tiles);
+        c->pb.ntiles = (int32_t*)(b + p_ntiles);
+        c->pb.h = (uint16_t*)(b + p_h);
+        c->pb.o = (float*)(b + p_o);
+    }
     if (hipMemset(c->scratch, 0, c->scratch_bytes) != hipSuccess ||
-        hipMemset(c->biases, 0, (size_t)L * g.E * 4) != hipSuccess) {
+        hipMemset(c->biases, 0, (size_t)L * g.E * 4) != hipSuccess ||
+        hipMemset(c->rstat, 0, (size_t)L * 2 * 4) != hipSuccess) {
         free_ctx(c);
         return fail(MOE_EHIP, "scratch initialisation failed");
     }
@@ -277,6 +323,9 @@ moe_status moe_load_experts(moe_ctx* c, const moe_layer_weights* w) {
             HIP_TRY(c, hipMemcpy(bdst, w->router_bias, (size_t)g.E * 4, hipMemcpyHostToDevice));
         else
             HIP_TRY(c, hipMemset(bdst, 0, (size_t)g.E * 4));
+        HIP_TRY(c, launch_router_stats(c->routers + (size_t)w->layer * g.E * g.H, bdst, g.E, g.H,
+                                       c->rstat + 2 * w->layer, c->load_stream));
+        HIP_TRY(c, hipStreamSynchronize(c->load_stream));
         c->router_loaded[w->layer] = 1;
     }
     if (w->expert_count > 0) {
@@ -352,6 +401,30 @@ moe_status route_decode(moe_ctx* c, int layer, const uint16_t* x, int T, int32_t
                  "top-k kernel launch");
 }
 
+moe_status route_prefill(moe_ctx* c, int layer, const uint16_t* x, int T, int32_t* trace_ids, float* trace_w,
+                         hipStream_t st, bool prof = false) {
+    const Geom& g = c->g;
+    const uint16_t* Wr = c->routers + (size_t)layer * g.E * g.H;
+    const float* bias = c->biases + (size_t)layer * g.E;
+    const float* rstat = c->rstat + 2 * layer;
+    moe_status s = timed(c, prof, MOE_K_PF_ROUTER, layer, st,
+                         [&](const Launch& lc) { return launch_pf_router(x, T, Wr, bias, g, c->pb, lc); },
+                         "prefill router kernel launch");
+    if (s != MOE_OK) return s;
+    s = timed(c, prof, MOE_K_PF_TOPK, layer, st, [&](const Launch& lc) {
+        return launch_pf_topk(x, T, Wr, bias, rstat, g, c->pb, trace_ids, trace_w, lc);
+    }, "prefill top-k kernel launch");
+    if (s != MOE_OK) return s;
+    s = timed(c, prof, MOE_K_PF_SORT, layer, st, [&](const Launch& lc) { return launch_pf_hist(T, g, c->pb, lc); },
+              "prefill histogram kernel launch");
+    if (s != MOE_OK) return s;
+    s = timed(c, prof, MOE_K_PF_SORT, layer, st, [&](const Launch& lc) { return launch_pf_scan(T, g, c->pb, lc); },
+              "prefill scan kernel launch");
+    if (s != MOE_OK) return s;
+    return timed(c, prof, MOE_K_PF_SORT, layer, st,
+                 [&](const Launch& lc) { return launch_pf_scatter(T, g, c->pb, lc); }, "prefill scatter kernel launch");
+}
+
 }  // namespace
 
 moe_status moe_route(moe_ctx* c, int32_t layer, const void* x, int32_t T, int32_t* ids, float* w, int32_t* offsets,
@@ -367,16 +440,19 @@ moe_status moe_route(moe_ctx* c, int32_t layer, const void* x, int32_t T, int32_
     if (!aligned16(x)) return fail(MOE_EINVAL, "x must be 16-byte aligned");
     moe_status s = check_layer_ready(c, layer, false);
     if (s != MOE_OK) return s;
-    if (T > kMaxDecodeT) return fail(MOE_EINVAL, "T %d: only windows of at most %d tokens are supported", T, kMaxDecodeT);
     hipStream_t st = (hipStream_t)hip_stream;
     HIP_TRY(c, hipSetDevice(c->cfg.device));
-    s = route_decode(c, layer, (const uint16_t*)x, T, nullptr, nullptr, st);
+    const bool pf = T > kMaxDecodeT;
+    s = pf ? route_prefill(c, layer, (const uint16_t*)x, T, nullptr, nullptr, st)
+           : route_decode(c, layer, (const uint16_t*)x, T, nullptr, nullptr, st);
     if (s != MOE_OK) return s;
     const size_t P = (size_t)T * g.k;
-    HIP_TRY(c, hipMemcpyAsync(ids, c->rb.ids, P * 4, hipMemcpyDeviceToDevice, st));
-    HIP_TRY(c, hipMemcpyAsync(w, c->rb.w, P * 4, hipMemcpyDeviceToDevice, st));
-    if (offsets) HIP_TRY(c, hipMemcpyAsync(offsets, c->rb.offsets, ((size_t)g.E + 1) * 4, hipMemcpyDeviceToDevice, st));
-    if (perm) HIP_TRY(c, hipMemcpyAsync(perm, c->rb.perm, P * 4, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(c, hipMemcpyAsync(ids, pf ? c->pb.ids : c->rb.ids, P * 4, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(c, hipMemcpyAsync(w, pf ? c->pb.w : c->rb.w, P * 4, hipMemcpyDeviceToDevice, st));
+    if (offsets)
+        HIP_TRY(c, hipMemcpyAsync(offsets, pf ? c->pb.offsets : c->rb.offsets, ((size_t)g.E + 1) * 4,
+                                  hipMemcpyDeviceToDevice, st));
+    if (perm) HIP_TRY(c, hipMemcpyAsync(perm, pf ? c->pb.perm : c->rb.perm, P * 4, hipMemcpyDeviceToDevice, st));
     return MOE_OK;
 }
 
@@ -399,7 +475,7 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
         if (s != MOE_OK) return s;
     }
     const int T = a->T;
-    if (T > kMaxDecodeT) return fail(MOE_EINVAL, "T %d: only windows of at most %d tokens are supported", T, kMaxDecodeT);
+    const bool pf = T > kMaxDecodeT;
     hipStream_t st = (hipStream_t)hip_stream;
     HIP_TRY(c, hipSetDevice(c->cfg.device));
     const int ES = g.E + g.S;
@@ -412,10 +488,28 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
         if (a->trace_x)
             HIP_TRY(c, hipMemcpyAsync((uint8_t*)a->trace_x + (size_t)i * xbytes, xin, xbytes, hipMemcpyDeviceToDevice, st));
         const bool prof = (a->flags & MOE_FWD_PROFILE) != 0;
-        moe_status s = route_decode(c, l, xin, T, a->trace_ids ? a->trace_ids + (size_t)i * T * g.k : nullptr,
-                                    a->trace_w ? a->trace_w + (size_t)i * T * g.k : nullptr, st, prof);
-        if (s != MOE_OK) return s;
         const uint8_t* slots = c->arena + (size_t)l * ES * g.slot_bytes;
+        int32_t* tids = a->trace_ids ? a->trace_ids + (size_t)i * T * g.k : nullptr;
+        float* tw = a->trace_w ? a->trace_w + (size_t)i * T * g.k : nullptr;
+        if (pf) {
+            moe_status s = route_prefill(c, l, xin, T, tids, tw, st, prof);
+            if (s != MOE_OK) return s;
+            s = timed(c, prof, MOE_K_PF_GEMM1, l, st,
+                      [&](const Launch& lc) { return launch_pf_gemm1(xin, slots, g, c->pb, lc); },
+                      "prefill gate/up GEMM launch");
+            if (s != MOE_OK) return s;
+            s = timed(c, prof, MOE_K_PF_GEMM2, l, st,
+                      [&](const Launch& lc) { return launch_pf_gemm2(slots, g, c->pb, lc); }, "prefill down GEMM launch");
+            if (s != MOE_OK) return s;
+            s = timed(c, prof, MOE_K_PF_COMBINE, l, st, [&](const Launch& lc) {
+                return launch_pf_combine(xin, T, g, c->pb, yout, a->flags & MOE_FWD_RESIDUAL, lc);
+            }, "prefill combine kernel launch");
+            if (s != MOE_OK) return s;
+            xin = yout;
+            continue;
+        }
+        moe_status s = route_decode(c, l, xin, T, tids, tw, st, prof);
+        if (s != MOE_OK) return s;
         s = timed(c, prof, MOE_K_GATEUP, l, st,
                   [&](const Launch& lc) { return launch_gateup_decode(xin, T, slots, g, c->rb, c->db, lc); },
                   "gate/up kernel launch");

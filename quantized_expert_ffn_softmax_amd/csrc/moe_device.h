@@ -1,0 +1,184 @@
+// Device helpers shared by the decode and prefill kernels of libmoe (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+// Launch on lc.st; with profiling events, the start/stop events are bound to the
+// dispatch itself (hipExtLaunchKernelGGL), so they time the kernel alone.
+template <class K, class... Args>
+inline void launch(K kernel, dim3 grid, dim3 block, uint32_t lds, const Launch& lc, Args... args) {
+    if (lc.start)
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, lc.st, lc.start, lc.stop, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, lc.st, args...);
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                   0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float h2f(uint32_t h16) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h16); }
+__device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
+__device__ __forceinline__ uint32_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ---------------------------------------------------------------- slot format
+// Offset constant of the bias trick: an operand value is 128 + q, the weight
+// is d*(q - o), so the contraction over a block is d*(R - (128+o)*S).
+template <int FMT> struct QF;
+template <> struct QF<1> { static constexpr float kBias = 136.0f; static constexpr int kCW = 16; };
+template <> struct QF<2> { static constexpr float kBias = 130.0f; static constexpr int kCW = 8; };
+
+// Block j (0..3) of a chunk as the MFMA B operand: four bf16 pairs (128+q).
+template <int FMT> __device__ __forceinline__ u32x4_t unpack(const uint32_t* cw, int j);
+template <> __device__ __forceinline__ u32x4_t unpack<1>(const uint32_t* cw, int j) {
+    const uint32_t w = cw[j];
+    u32x4_t r;
+    r.x = (w & 0x000F000Fu) | 0x43004300u;
+    r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+    r.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+    r.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    return r;
+}
+template <> __device__ __forceinline__ u32x4_t unpack<2>(const uint32_t* cw, int j) {
+    const uint32_t w = cw[j >> 1] >> (8 * (j & 1));
+    u32x4_t r;
+    r.x = (w & 0x00030003u) | 0x43004300u;
+    r.y = ((w >> 2) & 0x00030003u) | 0x43004300u;
+    r.z = ((w >> 4) & 0x00030003u) | 0x43004300u;
+    r.w = ((w >> 6) & 0x00030003u) | 0x43004300u;
+    return r;
+}
+
+template <int FMT> __device__ __forceinline__ void load_codes(const uint8_t* chunk, int lane, uint32_t* cw) {
+    if constexpr (FMT == 1) {
+        u32x4_t v = *reinterpret_cast<const u32x4_t*>(chunk + lane * 16);
+        cw[0] = v.x; cw[1] = v.y; cw[2] = v.z; cw[3] = v.w;
+    } else {
+        u32x2_t v = *reinterpret_cast<const u32x2_t*>(chunk + lane * 8);
+        cw[0] = v.x; cw[1] = v.y;
+    }
+}
+__device__ __forceinline__ u32x2_t load_scales(const uint8_t* chunk, int cw_bytes, int n) {
+    return *reinterpret_cast<const u32x2_t*>(chunk + 64 * cw_bytes + n * 8);
+}
+__device__ __forceinline__ float scale_of(u32x2_t s, int j) {
+    const uint32_t w = (j & 2) ? s.y : s.x;
+    return h2f((j & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+
+// ---------------------------------------------------------------- wave helpers
+// DPP lane permutations (GFX9 encodings): quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror.  Applied in this order, followed by xor 16 and
+// xor 32, every lane ends up combined with every other lane of the wave.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL> __device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL> __device__ __forceinline__ double dpp_f64(double v) {
+    const int lo = dpp<CTRL>(__double2loint(v)), hi = dpp<CTRL>(__double2hiint(v));
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v += dpp_f64<kDppXor1>(v);
+    v += dpp_f64<kDppXor2>(v);
+    v += dpp_f64<kDppHalfMirror>(v);
+    v += dpp_f64<kDppMirror>(v);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Total order of doubles as unsigned keys (-0 folded into +0).
+__device__ __forceinline__ uint64_t order_key(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v + 0.0);
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+__device__ __forceinline__ double key_value(uint64_t k) {
+    const uint64_t u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+    return __longlong_as_double((long long)u);
+}
+// (key, id) ordering of the selection: larger logit first, lower id on equal logits
+__device__ __forceinline__ bool ahead(uint64_t k1, int e1, uint64_t k2, int e2) {
+    return k1 > k2 || (k1 == k2 && e1 < e2);
+}
+template <int CTRL> __device__ __forceinline__ void argmax_step(uint64_t& k, int& e) {
+    const uint32_t lo = (uint32_t)dpp<CTRL>((int)(uint32_t)k);
+    const uint32_t hi = (uint32_t)dpp<CTRL>((int)(uint32_t)(k >> 32));
+    const int oe = dpp<CTRL>(e);
+    const uint64_t ok = ((uint64_t)hi << 32) | lo;
+    if (ahead(ok, oe, k, e)) { k = ok; e = oe; }
+}
+template <int CTRL, int ROWS> __device__ __forceinline__ void argmax_bcast(uint64_t& k, int& e) {
+    // lanes outside ROWS keep their own value (old = own), so the compare is a no-op there
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)k, (int)(uint32_t)k, CTRL, ROWS, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(k >> 32), (int)(uint32_t)(k >> 32), CTRL,
+                                                              ROWS, 0xF, false);
+    const int oe = __builtin_amdgcn_update_dpp(e, e, CTRL, ROWS, 0xF, false);
+    const uint64_t ok = ((uint64_t)hi << 32) | lo;
+    if (ahead(ok, oe, k, e)) { k = ok; e = oe; }
+}
+// Wave-wide best (key, id): row-level DPP butterflies, then row_bcast:15 and
+// row_bcast:31 carry the row winners into lane 63, which is read back as a
+// wave-uniform value.  Only VALU/DPP operations, no LDS round trips.
+__device__ __forceinline__ void wave_argmax(uint64_t& k, int& e) {
+    argmax_step<kDppXor1>(k, e);
+    argmax_step<kDppXor2>(k, e);
+    argmax_step<kDppHalfMirror>(k, e);
+    argmax_step<kDppMirror>(k, e);
+    argmax_bcast<0x142, 0xA>(k, e);  // row_bcast:15 into rows 1 and 3
+    argmax_bcast<0x143, 0xC>(k, e);  // row_bcast:31 into rows 2 and 3
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
+    e = __builtin_amdgcn_readlane(e, 63);
+    k = ((uint64_t)hi << 32) | lo;
+}
+
+// Raise a kernel's dynamic LDS limit when a launch needs more than the default.
+template <class K> hipError_t ensure_lds(K kernel, int bytes, int& granted) {
+    if (bytes <= granted) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) granted = bytes;
+    return e;
+}
+
+// Copy n16 16-byte elements from global memory to LDS with the whole
+// workgroup; every thread issues up to 8 loads before its first LDS store, so
+// the copy costs one memory latency.  dst_index maps a source element index
+// to its LDS element index (row padding).
+template <class Map>
+__device__ __forceinline__ void stage_lds(u32x4_t* dst, const u32x4_t* __restrict__ src, int n16, Map dst_index) {
+    for (int i0 = threadIdx.x; i0 < n16; i0 += blockDim.x * 8) {
+        u32x4_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = i0 + j * (int)blockDim.x;
+            if (i < n16) v[j] = src[i];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = i0 + j * (int)blockDim.x;
+            if (i < n16) dst[dst_index(i)] = v[j];
+        }
+    }
+}
+
+}  // namespace moe

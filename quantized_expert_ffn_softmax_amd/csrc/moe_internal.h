@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace moe {
 
 constexpr int kChunkBlocks = 4;
@@ -105,6 +107,32 @@ struct DecodeBufs {
 
 constexpr int kDownRowsPerWG = 128;  // 8 waves x 16 rows
 
+// Prefill scratch (T > kMaxDecodeT), sized for max_tokens.
+constexpr int kPfBlockTokens = 256;  // tokens per counting-sort block
+constexpr int kPfTileRows = 128;     // rows of one grouped-GEMM M-block
+struct PrefillBufs {
+    float* logits;     // [T x E]   fp32 MFMA logits (+ bias)
+    int32_t* ids;      // [T x k]
+    float* w;          // [T x k]
+    uint32_t* blkcnt;  // [nblk x E] pairs per (token block, expert)
+    int32_t* rank;     // [T x k]   rank of the pair inside its (block, expert) group
+    int32_t* offsets;  // [E + 1]
+    int32_t* perm;     // [T*k]
+    int32_t* inv;      // [T*k]
+    int32_t* rowtok;   // [T*k + S*T] token of each sorted row (routed rows by expert, then shared rows)
+    int32_t* blkbase;  // [nblk x E] first sorted position of the (block, expert) group
+    int32_t* tiles;    // [max_tiles x 4] (row0, nrows, group, 0)
+    int32_t* ntiles;   // [1]
+    uint16_t* h;       // [(T*k + S*T) x F] bf16 SwiGLU output in sorted row order
+    float* o;          // [(T*k + S*T) x H] fp32 per-row expert outputs
+    int max_tiles;
+};
+inline int prefill_max_tiles(int T, int k, int E, int S) {
+    const int64_t P = (int64_t)T * k;
+    return (int)((P + kPfTileRows - 1) / kPfTileRows + std::min<int64_t>(E, P) +
+                 (S ? (T + kPfTileRows - 1) / kPfTileRows : 0));
+}
+
 // Stream and optional profiling events of one launch.
 struct Launch {
     hipStream_t st;
@@ -123,5 +151,20 @@ hipError_t launch_down_decode(int T, const uint8_t* layer_slots, const Geom& g, 
                               const Launch& lc);
 hipError_t launch_combine_decode(const uint16_t* x, int T, const Geom& g, RouteBufs rb, DecodeBufs db, uint16_t* y,
                                  int residual, const Launch& lc);
+
+// Prefill launchers; rstat = {max_e ||W_r[e]||_2, max_e |b[e]|} of the layer's router.
+hipError_t launch_router_stats(const uint16_t* Wr, const float* bias, int E, int H, float* rstat, hipStream_t st);
+hipError_t launch_pf_router(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const Geom& g,
+                            PrefillBufs pb, const Launch& lc);
+hipError_t launch_pf_topk(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const float* rstat,
+                          const Geom& g, PrefillBufs pb, int32_t* trace_ids, float* trace_w, const Launch& lc);
+hipError_t launch_pf_hist(int T, const Geom& g, PrefillBufs pb, const Launch& lc);
+hipError_t launch_pf_scan(int T, const Geom& g, PrefillBufs pb, const Launch& lc);
+hipError_t launch_pf_scatter(int T, const Geom& g, PrefillBufs pb, const Launch& lc);
+hipError_t launch_pf_gemm1(const uint16_t* x, const uint8_t* layer_slots, const Geom& g, PrefillBufs pb,
+                           const Launch& lc);
+hipError_t launch_pf_gemm2(const uint8_t* layer_slots, const Geom& g, PrefillBufs pb, const Launch& lc);
+hipError_t launch_pf_combine(const uint16_t* x, int T, const Geom& g, PrefillBufs pb, uint16_t* y, int residual,
+                             const Launch& lc);
 
 }  // namespace moe

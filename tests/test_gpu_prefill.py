@@ -1,0 +1,200 @@
+"""GPU parity of the prefill path (T > 8: grouped GEMMs on MFMA) against the
+fp64 oracle, through the C ABI.
+
+Routing (ids, weights, offsets, perm) is compared for every token; y is
+compared over the whole [T x H] output at sizes the oracle finishes in
+seconds, and on a seeded sample of tokens for the 4096-token chunk (a token's
+output depends only on its own row, so the oracle evaluates the sampled rows
+alone).
+"""
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+import oracle
+from moe_inputs.configs import C1, C2, C5, MoEConfig, Q2B32, Q4B32
+
+from parity import (W_TOL, assert_y_close, bf16_dev_to_bits, bf16_dev_to_f64, load_layer, min_routing_gap,
+                    to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _check_routing(ctx, cfg, layer, xd, x, W, b, what):
+    ids, w, offsets, perm = ctx.route(layer, xd)
+    lg = oracle.router_logits(x, W, b)
+    ids_ref, w_ref = oracle.select_topk(lg, cfg.k)
+    off_ref, perm_ref, _, _ = oracle.permutation(ids_ref, cfg.E)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref, err_msg=f"{what}: ids")
+    np.testing.assert_array_equal(offsets.cpu().numpy(), off_ref, err_msg=f"{what}: offsets")
+    np.testing.assert_array_equal(perm.cpu().numpy(), perm_ref, err_msg=f"{what}: perm")
+    dw = float(np.abs(w.cpu().numpy().astype(np.float64) - w_ref).max())
+    assert dw <= W_TOL, f"{what}: weights differ by {dw:.2e}"
+    return lg, ids_ref, off_ref
+
+
+def _check_full(ctx, cfg, seed, layer, window, T, W, b, ex, what):
+    import torch
+    x = mi.gen_x(seed, window, T, cfg.H)
+    xd = to_dev_bf16(x)
+    print(f"[prefill] {what} seed={seed} layer={layer} T={T}", flush=True)
+    lg, _, off = _check_routing(ctx, cfg, layer, xd, x, W, b, what)
+    y = ctx.forward(xd, layer_begin=layer, layer_count=1)
+    torch.cuda.synchronize()
+    y_ref, _, _, _ = oracle.moe_layer(x, cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, cfg.fmt, W, b, ex, cfg.expert_bytes)
+    r, mx = assert_y_close(bf16_dev_to_f64(y), y_ref, what)
+    print(f"[prefill] {what}: rel-L2 {r:.2e} max-abs {mx:.2e} min-gap {min_routing_gap(lg, cfg.k):.2e} "
+          f"max rows/expert {int(np.diff(off).max())}", flush=True)
+    return y
+
+
+# Small shapes that still span several 128-row M-blocks, ragged N-tiles
+# (F = 160: 1.25 gate/up tiles; H = 640: 2.5 down tiles) and padded K chunks
+# (K/32 = 3 and 7 blocks).
+PF_Q4_SHARED = MoEConfig("pf_q4_shared", (1000,), 512, 256, 24, 1, 4, 2, Q4B32, mi.BIAS_NORMAL, 0.5)
+PF_Q2 = MoEConfig("pf_q2", (600,), 640, 160, 40, 0, 6, 1, Q2B32, mi.BIAS_ZIPF, 1.1)
+PF_ODD = MoEConfig("pf_odd", (300,), 96, 224, 7, 1, 3, 1, Q2B32, mi.BIAS_NONE, 0.0)
+PF_WIDE = MoEConfig("pf_wide", (200,), 256, 64, 1000, 0, 16, 1, Q4B32, mi.BIAS_ZIPF, 1.1)  # 16 logits per lane
+
+
+@pytest.mark.parametrize("cfg", [PF_Q4_SHARED, PF_Q2, PF_ODD, PF_WIDE], ids=lambda c: c.name)
+def test_small_prefill_full_output(torch_cuda, cfg):
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    T = cfg.T[0]
+    with MoEContext.from_config(cfg, max_tokens=T) as ctx:
+        for layer in range(cfg.L):
+            W, b, ex = load_layer(ctx, cfg, 7, layer)
+            _check_full(ctx, cfg, 7, layer, layer, T, W, b, ex, f"{cfg.name}/T{T}")
+
+
+@pytest.mark.parametrize("T", [9, 37, 128, 129, 257])
+def test_ragged_token_counts(torch_cuda, T):
+    """Prefill sizes just past the decode limit and around the 128-row M-block and 256-token sort block."""
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    cfg = PF_Q4_SHARED
+    with MoEContext.from_config(cfg, max_tokens=300, n_layers=1) as ctx:
+        W, b, ex = load_layer(ctx, cfg, 11, 0)
+        _check_full(ctx, cfg, 11, 0, T, T, W, b, ex, f"ragged/T{T}")
+
+
+def test_c1_shape_prefill(torch_cuda):
+    """The tiny shape (16 experts: one logit per lane) with a 64-token chunk."""
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    with MoEContext.from_config(C1, max_tokens=64) as ctx:
+        W, b, ex = load_layer(ctx, C1, 1, 0)
+        _check_full(ctx, C1, 1, 0, 3, 64, W, b, ex, "C1/T64")
+
+
+def test_c2_shape_prefill(torch_cuda):
+    """The Qwen-shaped layer (512 experts, q2b32, Zipf bias) with a 96-token chunk."""
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    with MoEContext.from_config(C2, max_tokens=96) as ctx:
+        W, b, ex = load_layer(ctx, C2, 1, 0)
+        _check_full(ctx, C2, 1, 0, 5, 96, W, b, ex, "C2/T96")
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_c5_prefill_chunk(torch_cuda, seed):
+    """4096 tokens x hidden 4096, 256+1 experts, top-6, q4b32: routing for every
+    token, y on 32 seeded tokens plus the first and last."""
+    import torch
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    cfg = C5
+    T = 4096
+    with MoEContext.from_config(cfg) as ctx:
+        W, b, ex = load_layer(ctx, cfg, seed, 0)
+        x = mi.gen_x(seed, 0, T, cfg.H)
+        xd = to_dev_bf16(x)
+        print(f"[prefill] C5 seed={seed}", flush=True)
+        lg, ids_ref, off = _check_routing(ctx, cfg, 0, xd, x, W, b, f"C5/seed{seed}")
+        counts = np.diff(off)
+        print(f"[prefill] C5 rows/expert max {counts.max()} mean {counts.mean():.1f}", flush=True)
+        y = ctx.forward(xd)
+        torch.cuda.synchronize()
+        yg = bf16_dev_to_f64(y)
+        rng = np.random.default_rng(seed)
+        sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 32, replace=False)]))
+        y_ref, ids_s, _, _ = oracle.moe_layer(np.ascontiguousarray(x[sample]), cfg.H, cfg.F, cfg.E, cfg.S, cfg.k,
+                                              cfg.fmt, W, b, ex, cfg.expert_bytes)
+        np.testing.assert_array_equal(ids_s, ids_ref[sample])
+        r, mx = assert_y_close(yg[sample], y_ref, f"C5/seed{seed} sampled")
+        print(f"[prefill] C5 seed={seed}: sampled rel-L2 {r:.2e} max-abs {mx:.2e}", flush=True)
+        # property at any size: y is finite and its rows are not all zero
+        assert np.isfinite(yg).all()
+        assert (np.abs(yg).max(axis=1) > 0).all()
+
+
+def test_prefill_chain_teacher_forced(torch_cuda):
+    """Two layers with the residual: each layer's traced input reproduces its
+    own single-layer output, and the chain's output is the residual sum."""
+    import torch
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    cfg = PF_Q4_SHARED
+    T = 150
+    with MoEContext.from_config(cfg, max_tokens=T) as ctx:
+        inputs = [load_layer(ctx, cfg, 13, layer) for layer in range(2)]
+        x = mi.gen_x(13, 0, T, cfg.H)
+        xd = to_dev_bf16(x)
+        y, tx, tids, tw = ctx.forward(xd, 0, 2, residual=True, trace=True)
+        torch.cuda.synchronize()
+        txb = bf16_dev_to_bits(tx)
+        np.testing.assert_array_equal(txb[0], x)
+        for layer, (W, b, ex) in enumerate(inputs):
+            y_ref, ids_ref, w_ref, _ = oracle.moe_layer(txb[layer], cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, cfg.fmt, W, b,
+                                                        ex, cfg.expert_bytes)
+            np.testing.assert_array_equal(tids[layer].cpu().numpy(), ids_ref)
+            assert np.abs(tw[layer].cpu().numpy() - w_ref).max() <= W_TOL
+            if layer == 0:
+                # layer 1's input is the residual stream bf16(x0 + y0), rounded once from fp32
+                assert_y_close(oracle.bf16_to_f64(txb[1]), oracle.bf16_to_f64(txb[0]) + y_ref, "residual stream")
+        y_last = oracle.moe_layer(txb[1], cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, cfg.fmt, *inputs[1], cfg.expert_bytes)[0]
+        y_ref = oracle.bf16_to_f64(txb[1]) + y_last
+        assert_y_close(bf16_dev_to_f64(y), y_ref, "prefill chain output")
+
+
+def test_prefill_determinism_bitwise(torch_cuda):
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    cfg = PF_Q2
+    with MoEContext.from_config(cfg, max_tokens=600) as ctx:
+        load_layer(ctx, cfg, 3, 0)
+        x = to_dev_bf16(mi.gen_x(3, 0, 600, cfg.H))
+        outs = [bf16_dev_to_bits(ctx.forward(x)) for _ in range(3)]
+        assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_prefill_tie_break(torch_cuda):
+    """Experts 3 and 11 with identical router rows and bias tie exactly for every token; the lower id wins."""
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    cfg = MoEConfig("tie_pf", (40,), 256, 64, 16, 0, 1, 1, Q4B32, mi.BIAS_NONE, 0.0)
+    W = mi.gen_router(5, 0, cfg.E, cfg.H)
+    W[11] = W[3]
+    bias = np.zeros(cfg.E, dtype=np.float32)
+    bias[3] = bias[11] = 50.0
+    ex = mi.gen_experts(5, 0, 0, cfg.E, cfg.H, cfg.F, cfg.fmt)
+    with MoEContext.from_config(cfg, max_tokens=40) as ctx:
+        ctx.load(0, router_w=W, router_bias=bias, experts=ex)
+        x = mi.gen_x(5, 0, 40, cfg.H)
+        ids, w, _, _ = ctx.route(0, to_dev_bf16(x))
+        assert ids.cpu().numpy().ravel().tolist() == [3] * 40
+        assert np.all(w.cpu().numpy() == 1.0)
+
+
+def test_decode_and_prefill_agree_on_routing(torch_cuda):
+    """T = 8 (decode kernels) and the same 8 rows inside a T = 16 call (prefill kernels) route identically."""
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    cfg = PF_Q2
+    with MoEContext.from_config(cfg, max_tokens=16) as ctx:
+        load_layer(ctx, cfg, 4, 0)
+        x = mi.gen_x(4, 0, 16, cfg.H)
+        ids8, w8, _, _ = ctx.route(0, to_dev_bf16(np.ascontiguousarray(x[:8])))
+        ids16, w16, _, _ = ctx.route(0, to_dev_bf16(x))
+        np.testing.assert_array_equal(ids8.cpu().numpy(), ids16.cpu().numpy()[:8])
+        assert np.abs(w8.cpu().numpy() - w16.cpu().numpy()[:8]).max() <= 1e-7
