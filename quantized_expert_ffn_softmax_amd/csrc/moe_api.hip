@@ -511,11 +511,11 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
         moe_status s = route_decode(c, l, xin, T, tids, tw, st, prof);
         if (s != MOE_OK) return s;
         s = timed(c, prof, MOE_K_GATEUP, l, st,
-                  [&](const Launch& lc) { return launch_gateup_decode(xin, T, slots, g, c->rb, c->db, lc); },
+                  [&](const Launch& lc) { return launch_gateup_decode(xin, T, slots, g, c->rb, c->db, c->maxA, lc); },
                   "gate/up kernel launch");
         if (s != MOE_OK) return s;
         s = timed(c, prof, MOE_K_DOWN, l, st,
-                  [&](const Launch& lc) { return launch_down_decode(T, slots, g, c->rb, c->db, lc); },
+                  [&](const Launch& lc) { return launch_down_decode(T, slots, g, c->rb, c->db, c->maxA, lc); },
                   "down kernel launch");
         if (s != MOE_OK) return s;
         s = timed(c, prof, MOE_K_COMBINE, l, st, [&](const Launch& lc) {

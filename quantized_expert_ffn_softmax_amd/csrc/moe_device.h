@@ -46,24 +46,33 @@ template <int FMT> struct QF;
 template <> struct QF<1> { static constexpr float kBias = 136.0f; static constexpr int kCW = 16; };
 template <> struct QF<2> { static constexpr float kBias = 130.0f; static constexpr int kCW = 8; };
 
+// The exponent bits 0x4300 of both bf16 halves, held in a VGPR.  The asm
+// only materialises the constant: as an opaque register value it lets each
+// (w & mask) | bits below become one v_and_or_b32 (VOP3 takes at most one
+// scalar or constant operand, which the mask uses).
+__device__ __forceinline__ uint32_t bf16_bias_bits() {
+    uint32_t k;
+    asm("v_mov_b32 %0, 0x43004300" : "=v"(k));
+    return k;
+}
 // Block j (0..3) of a chunk as the MFMA B operand: four bf16 pairs (128+q).
-template <int FMT> __device__ __forceinline__ u32x4_t unpack(const uint32_t* cw, int j);
-template <> __device__ __forceinline__ u32x4_t unpack<1>(const uint32_t* cw, int j) {
+template <int FMT> __device__ __forceinline__ u32x4_t unpack(const uint32_t* cw, int j, uint32_t k);
+template <> __device__ __forceinline__ u32x4_t unpack<1>(const uint32_t* cw, int j, uint32_t k) {
     const uint32_t w = cw[j];
     u32x4_t r;
-    r.x = (w & 0x000F000Fu) | 0x43004300u;
-    r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-    r.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-    r.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    r.x = (w & 0x000F000Fu) | k;
+    r.y = ((w >> 4) & 0x000F000Fu) | k;
+    r.z = ((w >> 8) & 0x000F000Fu) | k;
+    r.w = ((w >> 12) & 0x000F000Fu) | k;
     return r;
 }
-template <> __device__ __forceinline__ u32x4_t unpack<2>(const uint32_t* cw, int j) {
+template <> __device__ __forceinline__ u32x4_t unpack<2>(const uint32_t* cw, int j, uint32_t k) {
     const uint32_t w = cw[j >> 1] >> (8 * (j & 1));
     u32x4_t r;
-    r.x = (w & 0x00030003u) | 0x43004300u;
-    r.y = ((w >> 2) & 0x00030003u) | 0x43004300u;
-    r.z = ((w >> 4) & 0x00030003u) | 0x43004300u;
-    r.w = ((w >> 6) & 0x00030003u) | 0x43004300u;
+    r.x = (w & 0x00030003u) | k;
+    r.y = ((w >> 2) & 0x00030003u) | k;
+    r.z = ((w >> 4) & 0x00030003u) | k;
+    r.w = ((w >> 6) & 0x00030003u) | k;
     return r;
 }
 
@@ -96,6 +105,14 @@ template <int CTRL> __device__ __forceinline__ int dpp(int v) {
 template <int CTRL> __device__ __forceinline__ double dpp_f64(double v) {
     const int lo = dpp<CTRL>(__double2loint(v)), hi = dpp<CTRL>(__double2hiint(v));
     return __hiloint2double(hi, lo);
+}
+// Sum over the 16 lanes of each DPP row (every lane of the row gets it).
+__device__ __forceinline__ float row_sum_f32(float v) {
+    v += __int_as_float(dpp<kDppXor1>(__float_as_int(v)));
+    v += __int_as_float(dpp<kDppXor2>(__float_as_int(v)));
+    v += __int_as_float(dpp<kDppHalfMirror>(__float_as_int(v)));
+    v += __int_as_float(dpp<kDppMirror>(__float_as_int(v)));
+    return v;
 }
 __device__ __forceinline__ double wave_sum_f64(double v) {
     v += dpp_f64<kDppXor1>(v);
@@ -159,6 +176,31 @@ template <class K> hipError_t ensure_lds(K kernel, int bytes, int& granted) {
     if (e == hipSuccess) granted = bytes;
     return e;
 }
+
+// Two-step copy of n16 <= PER * blockDim.x 16-byte elements from global
+// memory to LDS: issue() requests every element into registers, commit()
+// stores them.  Loads and stores are unconditional (indices clamped; a slot
+// past the end, `dummy`, takes the stores of out-of-range lanes), so the code
+// is branch-free: loads the caller issues between the two steps (the
+// weights) keep exact wait counts and the stores wait for the staged elements
+// only.  A scheduling barrier after issue() keeps the staged loads first in
+// the memory queue.  n16 >= 1.
+template <int PER> struct StageRegs {
+    u32x4_t v[PER];
+    __device__ __forceinline__ void issue(const u32x4_t* __restrict__ src, int n16) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) v[j] = src[min((int)threadIdx.x + j * (int)blockDim.x, n16 - 1)];
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    template <class Map>
+    __device__ __forceinline__ void commit(u32x4_t* dst, int n16, Map dst_index, int dummy) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int i = (int)threadIdx.x + j * (int)blockDim.x;
+            dst[i < n16 ? dst_index(i) : dummy] = v[j];
+        }
+    }
+};
 
 // Copy n16 16-byte elements from global memory to LDS with the whole
 // workgroup; every thread issues up to 8 loads before its first LDS store, so

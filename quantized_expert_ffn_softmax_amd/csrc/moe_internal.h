@@ -146,8 +146,8 @@ hipError_t launch_router_decode(const uint16_t* x, int T, const uint16_t* Wr, co
 hipError_t launch_topk_sort_decode(int T, const Geom& g, RouteBufs rb, int32_t* trace_ids, float* trace_w,
                                    const Launch& lc);
 hipError_t launch_gateup_decode(const uint16_t* x, int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb,
-                                DecodeBufs db, const Launch& lc);
-hipError_t launch_down_decode(int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb, DecodeBufs db,
+                                DecodeBufs db, int maxA, const Launch& lc);
+hipError_t launch_down_decode(int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb, DecodeBufs db, int maxA,
                               const Launch& lc);
 hipError_t launch_combine_decode(const uint16_t* x, int T, const Geom& g, RouteBufs rb, DecodeBufs db, uint16_t* y,
                                  int residual, const Launch& lc);

@@ -8,10 +8,11 @@
 //                     weights, stable counting sort of the (token, expert)
 //                     pairs from per-expert token bitmasks, active-expert list
 //                     and weight table
-//   k_gateup_decode   per (active expert, 16-row tile of F): fused dequant +
-//                     gate/up GEMV on bf16 MFMA + SwiGLU; weights and x
-//                     fragments stream through a 4-chunk prefetch ring; writes
-//                     v = w * SwiGLU as bf16 hi/lo halves in MFMA-operand order
+//   k_gateup_decode   one workgroup per (active expert, 16-row tile of F):
+//                     fused dequant + gate/up GEMV on bf16 MFMA + SwiGLU; all
+//                     weight loads issued on entry, whole grid resident at
+//                     once; writes v = w * SwiGLU as bf16 hi/lo halves in
+//                     MFMA-operand order
 //   k_down_decode     per (active expert, 128-row group of H): down GEMV with
 //                     the expert's operand staged once in LDS; stores one
 //                     partial row block per expert
@@ -41,7 +42,7 @@ __device__ __forceinline__ void chunk_mac(const uint32_t* cw, u32x2_t sc, const 
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        f32x4_t R = mfma_bf16(A[j], unpack<FMT>(cw, j), zero);
+        f32x4_t R = mfma_bf16(A[j], unpack<FMT>(cw, j, bf16_bias_bits()), zero);
         const float d = scale_of(sc, j);
         acc[0] += d * R[0];
         acc[1] += d * R[1];
@@ -129,12 +130,15 @@ hipError_t launch_repack(const uint8_t* canon, uint8_t* slots, int count, const 
 // logits of expert 4b+w for every token.  Every bf16 x bf16 product is exact
 // in fp32 and is accumulated in fp64 (fixed reduction tree), so the selection
 // agrees with an fp64 evaluation except at logit gaps near 1e-15.
-// Each wave first issues all loads of its router row (up to 8 x 16 bytes per
-// lane per pass) while the workgroup stages x in LDS; one wait, then math.
+// The workgroup first requests its share of x (into registers), then every
+// wave requests its whole router row (up to 8 x 16 bytes per lane, H <= 4096);
+// x is written to LDS once it has arrived, while the row loads are still in
+// flight, and the math waits for each row load on its own.
 // All threads of the grid also share the per-block sums
 // sx[b][m] = sum_{q<32} x[m][32b+q] (fp32, in q order; zero for m >= T).
-constexpr int kRouterPass = 8;  // 16-byte loads per lane per pass: H <= 4096 in one pass
+constexpr int kRouterPass = 8;  // 16-byte loads per lane: H <= 4096
 
+template <int XPER>
 __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restrict__ x, int T,
                                                        const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
                                                        int E, int H, int nbp, double* __restrict__ logits,
@@ -145,41 +149,37 @@ __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restric
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int e = blockIdx.x * 4 + wave;
     const uint16_t* wrow = Wr + (int64_t)(e < E ? e : E - 1) * H;
+    const int n16 = T * (H / 8);
+    StageRegs<XPER> xst;
+    xst.issue(reinterpret_cast<const u32x4_t*>(x), n16);
+    u32x4_t wv[kRouterPass];
+#pragma unroll
+    for (int j = 0; j < kRouterPass; ++j) wv[j] = *reinterpret_cast<const u32x4_t*>(wrow + min((lane + 64 * j) * 8, H - 8));
+    __builtin_amdgcn_sched_barrier(0);
     const double be = bias ? (double)bias[e < E ? e : E - 1] : 0.0;
+    xst.commit(reinterpret_cast<u32x4_t*>(xs), n16, [](int i) { return i; }, n16);
+    __syncthreads();
     double acc[kMaxDecodeT];
 #pragma unroll
     for (int t = 0; t < kMaxDecodeT; ++t) acc[t] = 0.0;
-    for (int p0 = 0; p0 < H; p0 += 512 * kRouterPass) {
-        u32x4_t wv[kRouterPass];
 #pragma unroll
-        for (int j = 0; j < kRouterPass; ++j) {
-            const int h0 = p0 + (lane + 64 * j) * 8;
-            wv[j] = h0 < H ? *reinterpret_cast<const u32x4_t*>(wrow + h0) : u32x4_t{0u, 0u, 0u, 0u};
-        }
-        if (p0 == 0) {
-            stage_lds(reinterpret_cast<u32x4_t*>(xs), reinterpret_cast<const u32x4_t*>(x), T * (H / 8),
-                      [](int i) { return i; });
-            __syncthreads();
-        }
+    for (int j = 0; j < kRouterPass; ++j) {
+        const int h0 = (lane + 64 * j) * 8;
+        if (h0 < H) {
+            float wf[8];
 #pragma unroll
-        for (int j = 0; j < kRouterPass; ++j) {
-            const int h0 = p0 + (lane + 64 * j) * 8;
-            if (h0 < H) {
-                float wf[8];
+            for (int q = 0; q < 4; ++q) {
+                wf[2 * q] = __uint_as_float(wv[j][q] << 16);
+                wf[2 * q + 1] = __uint_as_float(wv[j][q] & 0xFFFF0000u);
+            }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    wf[2 * q] = __uint_as_float(wv[j][q] << 16);
-                    wf[2 * q + 1] = __uint_as_float(wv[j][q] & 0xFFFF0000u);
-                }
+            for (int t = 0; t < kMaxDecodeT; ++t) {
+                if (t < T) {
+                    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs + t * H + h0);
 #pragma unroll
-                for (int t = 0; t < kMaxDecodeT; ++t) {
-                    if (t < T) {
-                        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs + t * H + h0);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            acc[t] += (double)(__uint_as_float(xv[q] << 16) * wf[2 * q]);
-                            acc[t] += (double)(__uint_as_float(xv[q] & 0xFFFF0000u) * wf[2 * q + 1]);
-                        }
+                    for (int q = 0; q < 4; ++q) {
+                        acc[t] += (double)(__uint_as_float(xv[q] << 16) * wf[2 * q]);
+                        acc[t] += (double)(__uint_as_float(xv[q] & 0xFFFF0000u) * wf[2 * q + 1]);
                     }
                 }
             }
@@ -214,13 +214,21 @@ __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restric
 
 hipError_t launch_router_decode(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const Geom& g,
                                 RouteBufs rb, const Launch& lc) {
-    static int granted = 64 * 1024;
-    const int lds = T * g.H * 2;
-    hipError_t e = ensure_lds(k_router_decode, lds, granted);
-    if (e != hipSuccess) return e;
-    launch(k_router_decode, dim3((g.E + 3) / 4), dim3(256), lds, lc, x, T, Wr, bias, g.E, g.H,
-                       g.gu.nch * 4, rb.logits, rb.sx);
-    return hipGetLastError();
+    const int lds = T * g.H * 2 + 16;  // + the dummy slot of the staging stores
+    const int per = (T * (g.H / 8) + 255) / 256;  // <= 16 (T <= 8, H <= 4096)
+    const dim3 grid((g.E + 3) / 4);
+    hipError_t e;
+#define MOE_ROUTER_CASE(P)                                                                                       \
+    if (per <= P) {                                                                                              \
+        static int granted = 64 * 1024;                                                                          \
+        if ((e = ensure_lds(k_router_decode<P>, lds, granted)) != hipSuccess) return e;                          \
+        launch(k_router_decode<P>, grid, dim3(256), lds, lc, x, T, Wr, bias, g.E, g.H, g.gu.nch * 4, rb.logits,  \
+               rb.sx);                                                                                           \
+        return hipGetLastError();                                                                                \
+    }
+    MOE_ROUTER_CASE(2) MOE_ROUTER_CASE(4) MOE_ROUTER_CASE(8) MOE_ROUTER_CASE(16)
+#undef MOE_ROUTER_CASE
+    return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------- top-k + sort
@@ -357,217 +365,218 @@ hipError_t launch_topk_sort_decode(int T, const Geom& g, RouteBufs rb, int32_t* 
 }
 
 // ---------------------------------------------------------------- gate/up + SwiGLU
-// Persistent grid.  A work item is (active expert a, 16-row tile rt of F):
-// rows 16rt..16rt+15 of G and U.  The 4 waves of a workgroup split K = H into
-// contiguous ranges of at most NC chunks.  x is staged in LDS once per
-// workgroup.  Every wave keeps one register slot per chunk of its range: while
-// chunk j of the current item is multiplied, chunk j of the workgroup's next
-// item is requested into the same slot, so loads of one item overlap the
-// MFMAs of the previous one.  Loads are unconditional (indices clamped) so the
-// compiler can count them.  The MFMA computes C[m = token][n = row] with
-// A = x (rows m >= T zero).  Output: v = w_t,a * silu(g) * u as the bf16
-// hi/lo A fragments of the down projection, and their per-half-block sums.
-template <int FMT, int NC>
+// One workgroup per work item (active expert a, 16-row tile rt of F): rows
+// 16rt..16rt+15 of G and U.  The grid covers every item the call can have
+// (min(E, T k) + S experts), workgroups past the active count exit at once,
+// and the footprint is small enough that all items are resident together, so
+// every weight byte of the call is requested within the first microseconds.
+// The 4 waves split K = H into contiguous ranges of at most NC chunks and
+// issue all their loads on entry (unconditional, indices clamped, so the
+// compiler counts them) right after the workgroup's share of x, which is
+// written to LDS as soon as it arrives, with the weights still in flight.
+// The MFMA computes C[m = token][n = row] with A = x (rows m >= T zero).
+// Output: v = w_t,a * silu(g) * u as the bf16 hi/lo A fragments of the down
+// projection, and their per-half-block sums.
+// (slots and sx are deliberately not __restrict__: with it the compiler may
+// treat their loads as invariant and sink them past the barrier into the
+// branch that uses them, which serialises the weight stream behind staging.)
+template <int FMT, int NC, int XPER>
 __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restrict__ x, int T,
-                                                       const uint8_t* __restrict__ slots, Geom g,
-                                                       const float* __restrict__ sx, const int32_t* __restrict__ nact,
+                                                       const uint8_t* slots, Geom g,
+                                                       const float* sx, const int32_t* __restrict__ nact,
                                                        const int32_t* __restrict__ act, const float* __restrict__ wtab,
-                                                       uint32_t* __restrict__ afrag, float* __restrict__ spart) {
+                                                       int maxA, uint32_t* __restrict__ afrag,
+                                                       float* __restrict__ spart) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int rtn = g.F / 16;
-    const int items = nact[0] * rtn;
-    if ((int)blockIdx.x >= items) return;
+    const int a = blockIdx.x / rtn, rt = blockIdx.x - a * rtn;
+    const int na = nact[0];
+    const int e = act[min(a, maxA - 1)];  // requested together with nact
+    if (a >= na) return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, gs = lane >> 4, m = lane & 15;
     const MatGeom& mg = g.gu;
     const int c0 = wave * mg.nch / 4, c1 = (wave + 1) * mg.nch / 4;
     constexpr int CWN = FMT == 1 ? 4 : 2;
-    const int xstride = g.H + 8;
-    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [T][H + 8] (rows padded against bank conflicts)
-    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem + ((T * xstride * 2 + 15) / 16) * 16);  // [2][3][4][64]
-    __shared__ int32_t s_act[kMaxDecodeT * kMaxTopK + 1];
-    __shared__ float s_wt[(kMaxDecodeT * kMaxTopK + 1) * kMaxDecodeT];
-
+    const int64_t base = (int64_t)e * g.slot_bytes + (int64_t)rt * mg.tile_bytes;
+    const uint8_t* Gt = slots + base + g.g_off;
+    const uint8_t* Ut = slots + base + g.u_off;
+    const int h8 = g.H / 8, xs8 = h8 + 1;
+    StageRegs<XPER> xst;
+    xst.issue(reinterpret_cast<const u32x4_t*>(x), T * h8);
     uint32_t cg[NC][CWN], cu[NC][CWN];
     u32x2_t sg[NC], su[NC];
     float sxv[NC];
-    auto tiles = [&](int e, int rt, const uint8_t*& Gt, const uint8_t*& Ut) {
-        const int64_t base = (int64_t)e * g.slot_bytes + (int64_t)rt * mg.tile_bytes;
-        Gt = slots + base + g.g_off;
-        Ut = slots + base + g.u_off;
-    };
-    auto load = [&](const uint8_t* Gt, const uint8_t* Ut, int j) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) sxv[j] = sx[(min(c0 + j, mg.nch - 1) * 4 + gs) * 16 + m];
+    __builtin_amdgcn_sched_barrier(0);
+    // chunk by chunk (scheduling barriers keep the order), so the math on
+    // chunk j can start as soon as chunk j has arrived
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
         const int c = min(c0 + j, mg.nch - 1);
         const int64_t off = (int64_t)c * mg.chunk_bytes;
         load_codes<FMT>(Gt + off, lane, cg[j]);
-        load_codes<FMT>(Ut + off, lane, cu[j]);
         sg[j] = load_scales(Gt + off, QF<FMT>::kCW, n);
+        load_codes<FMT>(Ut + off, lane, cu[j]);
         su[j] = load_scales(Ut + off, QF<FMT>::kCW, n);
-        sxv[j] = sx[(c * 4 + gs) * 16 + m];
-    };
-    int it = blockIdx.x;
-    const uint8_t *Gt, *Ut;
-    tiles(act[it / rtn], it % rtn, Gt, Ut);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // routing weights of this expert's tokens (used by wave 0 in the epilogue)
+    const f32x4_t wt0 = *reinterpret_cast<const f32x4_t*>(wtab + a * kMaxDecodeT);
+    const f32x4_t wt1 = *reinterpret_cast<const f32x4_t*>(wtab + a * kMaxDecodeT + 4);
+    const int xstride = g.H + 8;
+    // [T + 1][H + 8]: rows padded against bank conflicts; row T is zero and is
+    // what the MFMA rows m >= T read, so the A operands need no masking
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
-    for (int j = 0; j < NC; ++j) load(Gt, Ut, j);
+    for (int j = 0; j < 3; ++j) {  // xs8 <= 513 elements of 16 bytes
+        const int i = threadIdx.x + 256 * j;
+        if (i < xs8) reinterpret_cast<u32x4_t*>(xs)[T * xs8 + i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
     {
-        const int nA = nact[0];
-        for (int i = threadIdx.x; i < nA; i += blockDim.x) s_act[i] = act[i];
-        for (int i = threadIdx.x; i < nA * kMaxDecodeT; i += blockDim.x) s_wt[i] = wtab[i];
-        const int h8 = g.H / 8, xs8 = xstride / 8;
-        stage_lds(reinterpret_cast<u32x4_t*>(xs), reinterpret_cast<const u32x4_t*>(x), T * h8, [=](int q) {
-            const int t = q / h8;
-            return t * xs8 + (q - t * h8);
-        });
+        const float inv_h8 = 1.0f / (float)h8;  // q < 4096, h8 <= 512: (q + 0.5) / h8 is never within 1e-3 of an integer
+        // element q of row t lands at q + t (rows are h8 + 1 elements apart in LDS)
+        xst.commit(reinterpret_cast<u32x4_t*>(xs), T * h8, [=](int q) {
+            return q + (int)(((float)q + 0.5f) * inv_h8);
+        }, (T + 1) * xs8);
     }
     __syncthreads();
-    const bool xrow = m < T;
-    const uint16_t* xl = xs + m * xstride + 8 * gs;
-    int buf = 0;
-    for (; it < items; it += gridDim.x, buf ^= 1) {
-        const int a = it / rtn, rt = it - a * rtn;
-        const int nx = it + (int)gridDim.x < items ? it + (int)gridDim.x : it;
-        const uint8_t *Gn, *Un;
-        tiles(s_act[nx / rtn], nx % rtn, Gn, Un);
-        f32x4_t accG = {0.f, 0.f, 0.f, 0.f}, accU = accG, corG = accG, corU = accG;
+    const uint16_t* xl = xs + (m < T ? m : T) * xstride + 8 * gs;
+    f32x4_t accG = {0.f, 0.f, 0.f, 0.f}, accU = accG, corG = accG, corU = accG;
 #pragma unroll
-        for (int j = 0; j < NC; ++j) {
-            const int c = c0 + j;
-            if (c < c1) {
-                u32x4_t A[4];
+    for (int j = 0; j < NC; ++j) {
+        const int c = c0 + j;
+        if (c < c1) {
+            // blocks past nb (K padding) have zero scales and zero block sums:
+            // any finite operand works, so the block index is clamped
+            u32x4_t A[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int b = c * 4 + q;
-                    A[q] = (xrow && b < mg.nb) ? *reinterpret_cast<const u32x4_t*>(xl + b * 32) : u32x4_t{0u, 0u, 0u, 0u};
-                }
-                chunk_mac<FMT>(cg[j], sg[j], A, sxv[j], gs, accG, corG);
-                chunk_mac<FMT>(cu[j], su[j], A, sxv[j], gs, accU, corU);
-            }
-            load(Gn, Un, j);  // chunk j of the next item (a repeat of this one after the last item)
-        }
-        // waves 1..3 hand their partial sums to wave 0 (double-buffered: one barrier per item)
-        f32x4_t* rb2 = red + buf * 3 * 4 * 64;
-        if (wave > 0) {
-            rb2[((wave - 1) * 4 + 0) * 64 + lane] = accG;
-            rb2[((wave - 1) * 4 + 1) * 64 + lane] = accU;
-            rb2[((wave - 1) * 4 + 2) * 64 + lane] = corG;
-            rb2[((wave - 1) * 4 + 3) * 64 + lane] = corU;
-        }
-        __syncthreads();
-        if (wave == 0) {
-#pragma unroll
-            for (int w = 0; w < 3; ++w) {
-                accG += rb2[(w * 4 + 0) * 64 + lane];
-                accU += rb2[(w * 4 + 1) * 64 + lane];
-                corG += rb2[(w * 4 + 2) * 64 + lane];
-                corU += rb2[(w * 4 + 3) * 64 + lane];
-            }
-            // lane holds (token t = 4*gs + i, row f = 16*rt + n); tokens < 8 live in gs 0..1.
-            // v = w * silu(g) * u becomes the down projection's A operand: rows m = t
-            // (bf16 hi) and 8 + t (bf16 lo), k = f, in the layout of one MFMA fragment
-            // per 32-wide block of F, plus the per-half-block row sums of both halves.
-            const int nbFp = g.dn.nch * 4;
-            const int bF = rt >> 1, kf = 16 * (rt & 1) + n;
-            uint16_t* af16 = reinterpret_cast<uint16_t*>(afrag) + ((int64_t)a * nbFp + bF) * 64 * 8;
-            float shi[4], slo[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 4 * gs + i;
-                const float gv = accG[i] - QF<FMT>::kBias * corG[i];
-                const float uv = accU[i] - QF<FMT>::kBias * corU[i];
-                const float h = gv / (1.0f + expf(-gv)) * uv;
-                const float v = (t < T ? s_wt[a * kMaxDecodeT + t] : 0.f) * h;
-                const uint32_t hi = f2bf(v);
-                const uint32_t lo = f2bf(v - bf2f(hi));
-                shi[i] = bf2f(hi);
-                slo[i] = bf2f(lo);
-                if (t < T) {
-                    af16[(t + 16 * (kf >> 3)) * 8 + (kf & 7)] = (uint16_t)hi;
-                    af16[(8 + t + 16 * (kf >> 3)) * 8 + (kf & 7)] = (uint16_t)lo;
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) {
-                    shi[i] += __shfl_xor(shi[i], off);
-                    slo[i] += __shfl_xor(slo[i], off);
-                }
-            }
-            if (n == 0 && gs < 2) {
-                float* sp = spart + (((int64_t)a * nbFp + bF) * 2 + (rt & 1)) * 16;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 4 * gs + i;
-                    if (t < T) {
-                        sp[t] = shi[i];
-                        sp[8 + t] = slo[i];
-                    }
-                }
-            }
+            for (int q = 0; q < 4; ++q)
+                A[q] = *reinterpret_cast<const u32x4_t*>(xl + min(c * 4 + q, mg.nb - 1) * 32);
+            chunk_mac<FMT>(cg[j], sg[j], A, sxv[j], gs, accG, corG);
+            chunk_mac<FMT>(cu[j], su[j], A, sxv[j], gs, accU, corU);
         }
     }
+    // waves 1..3 hand their partial sums to wave 0 through the LDS area x occupied
+    __syncthreads();
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem);  // [3][4][64]
+    if (wave > 0) {
+        red[((wave - 1) * 4 + 0) * 64 + lane] = accG;
+        red[((wave - 1) * 4 + 1) * 64 + lane] = accU;
+        red[((wave - 1) * 4 + 2) * 64 + lane] = corG;
+        red[((wave - 1) * 4 + 3) * 64 + lane] = corU;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+        accG += red[(w * 4 + 0) * 64 + lane];
+        accU += red[(w * 4 + 1) * 64 + lane];
+        corG += red[(w * 4 + 2) * 64 + lane];
+        corU += red[(w * 4 + 3) * 64 + lane];
+    }
+    // lane holds (token t = 4*gs + i, row f = 16*rt + n); tokens < 8 live in gs 0..1.
+    // v = w * silu(g) * u becomes the down projection's A operand: rows m = t
+    // (bf16 hi) and 8 + t (bf16 lo), k = f, in the layout of one MFMA fragment
+    // per 32-wide block of F, plus the per-half-block row sums of both halves.
+    const int nbFp = g.dn.nch * 4;
+    const int bF = rt >> 1, kf = 16 * (rt & 1) + n;
+    uint16_t* af16 = reinterpret_cast<uint16_t*>(afrag) + ((int64_t)a * nbFp + bF) * 64 * 8;
+    float shi[4], slo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = 4 * gs + i;
+        const float gv = accG[i] - QF<FMT>::kBias * corG[i];
+        const float uv = accU[i] - QF<FMT>::kBias * corU[i];
+        const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+        const float wv = gs == 0 ? wt0[i] : wt1[i];
+        const float v = t < T ? wv * h : 0.f;  // rows t >= T are written as zeros
+        const uint32_t hi = f2bf(v);
+        const uint32_t lo = f2bf(v - bf2f(hi));
+        shi[i] = bf2f(hi);
+        slo[i] = bf2f(lo);
+        if (gs < 2) {
+            af16[(t + 16 * (kf >> 3)) * 8 + (kf & 7)] = (uint16_t)hi;
+            af16[(8 + t + 16 * (kf >> 3)) * 8 + (kf & 7)] = (uint16_t)lo;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        shi[i] = row_sum_f32(shi[i]);
+        slo[i] = row_sum_f32(slo[i]);
+    }
+    if (n == 0 && gs < 2) {
+        float* sp = spart + (((int64_t)a * nbFp + bF) * 2 + (rt & 1)) * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * gs + i;
+            sp[t] = shi[i];
+            sp[8 + t] = slo[i];
+        }
+    }
+}
+
+template <int FMT, int NC, int XPER>
+hipError_t launch_gateup_x(const uint16_t* x, int T, const uint8_t* slots, const Geom& g, RouteBufs rb,
+                           DecodeBufs db, int maxA_T, int maxA, const Launch& lc) {
+    static int granted = 64 * 1024;
+    const int xbytes = (T + 1) * (g.H + 8) * 2 + 16;  // + the zero row and the dummy slot of the staging stores
+    const int lds = xbytes > 3 * 4 * 64 * 16 ? xbytes : 3 * 4 * 64 * 16;
+    hipError_t e = ensure_lds(k_gateup_decode<FMT, NC, XPER>, lds, granted);
+    if (e != hipSuccess) return e;
+    launch(k_gateup_decode<FMT, NC, XPER>, dim3(maxA_T * (g.F / 16)), dim3(256), lds, lc, x, T, slots, g, rb.sx,
+           rb.nact, rb.act, rb.wtab, maxA, db.afrag, db.spart);
+    return hipGetLastError();
 }
 
 template <int FMT, int NC>
 hipError_t launch_gateup_nc(const uint16_t* x, int T, const uint8_t* slots, const Geom& g, RouteBufs rb,
-                            DecodeBufs db, int max_items, const Launch& lc) {
-    static int granted = 64 * 1024;
-    static int per_cu[2 * kMaxDecodeT + 1] = {0};  // resident workgroups per CU, by T
-    const int lds = ((T * (g.H + 8) * 2 + 15) / 16) * 16 + 2 * 3 * 4 * 64 * 16;
-    hipError_t e = ensure_lds(k_gateup_decode<FMT, NC>, lds, granted);
-    if (e != hipSuccess) return e;
-    if (per_cu[T] == 0) {
-        int nb = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_gateup_decode<FMT, NC>, 256, lds);
-        if (e != hipSuccess) return e;
-        per_cu[T] = nb > 0 ? nb : 1;
-    }
-    int dev = 0, cus = 0;
-    hipGetDevice(&dev);
-    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    int grid = per_cu[T] * cus;
-    if (grid > max_items) grid = max_items;
-    launch(k_gateup_decode<FMT, NC>, dim3(grid), dim3(256), lds, lc, x, T, slots, g, rb.sx, rb.nact,
-                       rb.act, rb.wtab, db.afrag, db.spart);
-    return hipGetLastError();
+                            DecodeBufs db, int maxA_T, int maxA, const Launch& lc) {
+    const int per = (T * (g.H / 8) + 255) / 256;  // <= 16
+    if (per <= 2) return launch_gateup_x<FMT, NC, 2>(x, T, slots, g, rb, db, maxA_T, maxA, lc);
+    if (per <= 4) return launch_gateup_x<FMT, NC, 4>(x, T, slots, g, rb, db, maxA_T, maxA, lc);
+    if (per <= 5) return launch_gateup_x<FMT, NC, 5>(x, T, slots, g, rb, db, maxA_T, maxA, lc);
+    if (per <= 8) return launch_gateup_x<FMT, NC, 8>(x, T, slots, g, rb, db, maxA_T, maxA, lc);
+    return launch_gateup_x<FMT, NC, 16>(x, T, slots, g, rb, db, maxA_T, maxA, lc);
 }
 
 hipError_t launch_gateup_decode(const uint16_t* x, int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb,
-                                DecodeBufs db, const Launch& lc) {
-    const int maxA = (g.E < T * g.k ? g.E : T * g.k) + g.S;
-    const int max_items = maxA * (g.F / 16);
+                                DecodeBufs db, int maxA, const Launch& lc) {
+    const int maxA_T = (g.E < T * g.k ? g.E : T * g.k) + g.S;
     const int per_wave = (g.gu.nch + 3) / 4;
+#define MOE_GATEUP_CASE(F, N) \
+    if (per_wave <= N) return launch_gateup_nc<F, N>(x, T, layer_slots, g, rb, db, maxA_T, maxA, lc);
     if (g.fmt == 1) {
-        if (per_wave <= 2) return launch_gateup_nc<1, 2>(x, T, layer_slots, g, rb, db, max_items, lc);
-        if (per_wave <= 4) return launch_gateup_nc<1, 4>(x, T, layer_slots, g, rb, db, max_items, lc);
-        if (per_wave <= 6) return launch_gateup_nc<1, 6>(x, T, layer_slots, g, rb, db, max_items, lc);
-        return launch_gateup_nc<1, 8>(x, T, layer_slots, g, rb, db, max_items, lc);
+        MOE_GATEUP_CASE(1, 2) MOE_GATEUP_CASE(1, 3) MOE_GATEUP_CASE(1, 4) MOE_GATEUP_CASE(1, 5)
+        MOE_GATEUP_CASE(1, 6) return launch_gateup_nc<1, 8>(x, T, layer_slots, g, rb, db, maxA_T, maxA, lc);
     }
-    if (per_wave <= 2) return launch_gateup_nc<2, 2>(x, T, layer_slots, g, rb, db, max_items, lc);
-    if (per_wave <= 4) return launch_gateup_nc<2, 4>(x, T, layer_slots, g, rb, db, max_items, lc);
-    if (per_wave <= 6) return launch_gateup_nc<2, 6>(x, T, layer_slots, g, rb, db, max_items, lc);
-    return launch_gateup_nc<2, 8>(x, T, layer_slots, g, rb, db, max_items, lc);
+    MOE_GATEUP_CASE(2, 2) MOE_GATEUP_CASE(2, 3) MOE_GATEUP_CASE(2, 4) MOE_GATEUP_CASE(2, 5)
+    MOE_GATEUP_CASE(2, 6) return launch_gateup_nc<2, 8>(x, T, layer_slots, g, rb, db, maxA_T, maxA, lc);
+#undef MOE_GATEUP_CASE
 }
 
 // ---------------------------------------------------------------- down projection
-constexpr int kRing = 4;  // chunks in flight per wave beyond the one being multiplied
+constexpr int kRing = 8;  // chunks in flight per wave beyond the one being multiplied
 
-// Grid (ceil(H/128), maxA), 512 threads.  Workgroup (rg, a) computes the down
-// projection of active expert a for rows 128rg..128rg+127 (wave w: row tile
-// 8rg+w).  Each wave issues every weight load of its row tile (at most NC
-// chunks per pass), then the workgroup copies the expert's A fragments
-// (v hi rows 0..7 | v lo rows 8..15) into LDS; one wait, then the MFMAs.
-// Output: part[a][t][row].
-template <int FMT, int NC>
-__global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* __restrict__ slots, Geom g,
+// Grid (ceil(H/128), min(E, T k) + S), 512 threads.  Workgroup (rg, a)
+// computes the down projection of active expert a for rows 128rg..128rg+127
+// (wave w: row tile 8rg+w).  The workgroup first requests the expert's A
+// fragments (v hi rows 0..7 | v lo rows 8..15), then each wave requests the
+// first kRing chunks of its row tile; the fragments go to LDS as soon as they
+// arrive and every further chunk is requested as one is consumed.  K = F fits
+// one pass (nch <= NC).  Output: part[a][t][row].
+template <int FMT, int NC, int FPER>
+__global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots, Geom g,
                                                      const int32_t* __restrict__ nact, const int32_t* __restrict__ act,
-                                                     const uint32_t* __restrict__ afrag,
-                                                     const float* __restrict__ spart, float* __restrict__ part) {
+                                                     int maxA, const uint32_t* __restrict__ afrag,
+                                                     const float* spart, float* __restrict__ part) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int a = blockIdx.y;
-    if (a >= nact[0]) return;
+    const int na = nact[0];
+    const int e = act[min(a, maxA - 1)];  // requested together with nact
+    if (a >= na) return;
     const int rg = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, gs = lane >> 4, m = lane & 15;
@@ -575,53 +584,56 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* __res
     const int nbp = md.nch * 4;
     const int rt = rg * 8 + wave;
     const bool live = rt < g.H / 16;
-    const int e = act[a];
     const uint8_t* Dt = slots + (int64_t)e * g.slot_bytes + g.d_off + (int64_t)(live ? rt : 0) * md.tile_bytes;
     constexpr int CWN = FMT == 1 ? 4 : 2;
     u32x4_t* frag = reinterpret_cast<u32x4_t*>(smem);
-    const bool mrow = (m & 7) < T;
+    StageRegs<FPER> fst;
+    fst.issue(reinterpret_cast<const u32x4_t*>(afrag) + (int64_t)a * nbp * 64, nbp * 64);
     const float* sp = spart + (int64_t)a * nbp * 32;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, corr = acc;
-    constexpr int R = NC < kRing ? NC : kRing;
+    // ring depth: kRing chunks, 6 for the 16-chunk q4 case (register budget)
+    constexpr int R = NC < kRing ? NC : (FMT == 1 && NC > 8 ? 6 : kRing);
     uint32_t cw[R][CWN];
     u32x2_t sc[R];
-    float s0[R], s1[R];
-    // ring of kRing chunks with unconditional (clamped) loads, fully unrolled over NC
+    float s0[NC], s1[NC];
+    // block sums of the fragment rows first (small, from L2), then a ring of R
+    // chunks with unconditional (clamped) loads, fully unrolled over NC
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int bq = min(c, md.nch - 1) * 4 + gs;
+        s0[c] = sp[bq * 32 + m];
+        s1[c] = sp[bq * 32 + 16 + m];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     auto load = [&](int c, int i) {
-        c = min(c, md.nch - 1);
-        const int64_t off = (int64_t)c * md.chunk_bytes;
+        const int cc = min(c, md.nch - 1);
+        const int64_t off = (int64_t)cc * md.chunk_bytes;
         load_codes<FMT>(Dt + off, lane, cw[i]);
         sc[i] = load_scales(Dt + off, QF<FMT>::kCW, n);
-        const int bq = c * 4 + gs;
-        s0[i] = sp[bq * 32 + m];
-        s1[i] = sp[bq * 32 + 16 + m];
     };
+    // The fragments of all 8 token rows (zeros for t >= T) and of the padded
+    // blocks (zeros, never written) are defined, so nothing is masked; chunks
+    // past nch (NC > nch) carry zero scales and add nothing.
     auto compute = [&](int c, int i) {
         u32x4_t A[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int b = c * 4 + j;
-            A[j] = (mrow && b < md.nb) ? frag[b * 64 + lane] : u32x4_t{0u, 0u, 0u, 0u};
-        }
-        const int bq = c * 4 + gs;
-        const float s = (mrow && bq < md.nb) ? s0[i] + s1[i] : 0.f;
-        chunk_mac<FMT>(cw[i], sc[i], A, s, gs, acc, corr);
+        for (int j = 0; j < 4; ++j) A[j] = frag[min(c * 4 + j, nbp - 1) * 64 + lane];
+        const u32x2_t scc = c < md.nch ? sc[i] : u32x2_t{0u, 0u};  // padding chunk (NC > nch): zero scales
+        chunk_mac<FMT>(cw[i], scc, A, s0[c] + s1[c], gs, acc, corr);
     };
-    for (int cb = 0; cb < md.nch; cb += NC) {
 #pragma unroll
-        for (int i = 0; i < R; ++i) load(cb + i, i);
-        if (cb == 0) {
-            stage_lds(frag, reinterpret_cast<const u32x4_t*>(afrag) + (int64_t)a * nbp * 64, nbp * 64,
-                      [](int q) { return q; });
-            __syncthreads();
-        }
-        if (live) {
+    for (int i = 0; i < R; ++i) {
+        load(i, i);
+        __builtin_amdgcn_sched_barrier(0);  // chunk order kept: the math on chunk i waits for chunk i only
+    }
+    fst.commit(frag, nbp * 64, [](int q) { return q; }, nbp * 64);
+    __syncthreads();
+    // waves past the last row tile compute on tile 0 and discard the result:
+    // no branch around the refill loads
 #pragma unroll
-            for (int i = 0; i < NC; ++i) {
-                if (cb + i < md.nch) compute(cb + i, i % R);
-                if (i + R < NC) load(cb + i + R, i % R);
-            }
-        }
+    for (int i = 0; i < NC; ++i) {
+        compute(i, i % R);
+        if (i + R < NC) load(i + R, i % R);
     }
     if (!live) return;
     f32x4_t v;
@@ -639,31 +651,41 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* __res
     }
 }
 
-template <int FMT, int NC>
-hipError_t launch_down_nc(int T, const uint8_t* slots, const Geom& g, RouteBufs rb, DecodeBufs db, dim3 grid, int lds,
-                          const Launch& lc) {
+template <int FMT, int NC, int FPER>
+hipError_t launch_down_f(int T, const uint8_t* slots, const Geom& g, RouteBufs rb, DecodeBufs db, dim3 grid, int lds,
+                         int maxA, const Launch& lc) {
     static int granted = 64 * 1024;
-    hipError_t e = ensure_lds(k_down_decode<FMT, NC>, lds, granted);
+    hipError_t e = ensure_lds(k_down_decode<FMT, NC, FPER>, lds, granted);
     if (e != hipSuccess) return e;
-    launch(k_down_decode<FMT, NC>, grid, dim3(512), lds, lc, T, slots, g, rb.nact, rb.act, db.afrag,
-                       db.spart, db.part);
+    launch(k_down_decode<FMT, NC, FPER>, grid, dim3(512), lds, lc, T, slots, g, rb.nact, rb.act, maxA, db.afrag,
+           db.spart, db.part);
     return hipGetLastError();
 }
 
-hipError_t launch_down_decode(int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb, DecodeBufs db,
+template <int FMT, int NC>
+hipError_t launch_down_nc(int T, const uint8_t* slots, const Geom& g, RouteBufs rb, DecodeBufs db, dim3 grid, int lds,
+                          int maxA, const Launch& lc) {
+    const int per = (g.dn.nch * 4 * 64 + 511) / 512;  // <= 8 (F <= 2048)
+    if (per <= 2) return launch_down_f<FMT, NC, 2>(T, slots, g, rb, db, grid, lds, maxA, lc);
+    if (per <= 4) return launch_down_f<FMT, NC, 4>(T, slots, g, rb, db, grid, lds, maxA, lc);
+    return launch_down_f<FMT, NC, 8>(T, slots, g, rb, db, grid, lds, maxA, lc);
+}
+
+hipError_t launch_down_decode(int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb, DecodeBufs db, int maxA,
                               const Launch& lc) {
-    const int maxA = (g.E < T * g.k ? g.E : T * g.k) + g.S;
-    const int lds = g.dn.nch * 4 * 64 * 16;
-    dim3 grid((g.H + kDownRowsPerWG - 1) / kDownRowsPerWG, maxA);
-    const int nch = g.dn.nch;
+    const int maxA_T = (g.E < T * g.k ? g.E : T * g.k) + g.S;
+    const int lds = g.dn.nch * 4 * 64 * 16 + 16;  // + the dummy slot of the staging stores
+    dim3 grid((g.H + kDownRowsPerWG - 1) / kDownRowsPerWG, maxA_T);
+    const int nch = g.dn.nch;  // <= 16 (F <= 2048)
+#define MOE_DOWN_CASE(F, N) \
+    if (nch <= N) return launch_down_nc<F, N>(T, layer_slots, g, rb, db, grid, lds, maxA, lc);
     if (g.fmt == 1) {
-        if (nch <= 4) return launch_down_nc<1, 4>(T, layer_slots, g, rb, db, grid, lds, lc);
-        if (nch <= 8) return launch_down_nc<1, 8>(T, layer_slots, g, rb, db, grid, lds, lc);
-        return launch_down_nc<1, 16>(T, layer_slots, g, rb, db, grid, lds, lc);
+        MOE_DOWN_CASE(1, 2) MOE_DOWN_CASE(1, 4) MOE_DOWN_CASE(1, 5) MOE_DOWN_CASE(1, 8)
+        return launch_down_nc<1, 16>(T, layer_slots, g, rb, db, grid, lds, maxA, lc);
     }
-    if (nch <= 4) return launch_down_nc<2, 4>(T, layer_slots, g, rb, db, grid, lds, lc);
-    if (nch <= 8) return launch_down_nc<2, 8>(T, layer_slots, g, rb, db, grid, lds, lc);
-    return launch_down_nc<2, 16>(T, layer_slots, g, rb, db, grid, lds, lc);
+    MOE_DOWN_CASE(2, 2) MOE_DOWN_CASE(2, 4) MOE_DOWN_CASE(2, 5) MOE_DOWN_CASE(2, 8)
+    return launch_down_nc<2, 16>(T, layer_slots, g, rb, db, grid, lds, maxA, lc);
+#undef MOE_DOWN_CASE
 }
 
 // ---------------------------------------------------------------- combine
