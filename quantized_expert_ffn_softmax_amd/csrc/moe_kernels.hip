@@ -591,23 +591,19 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots
     fst.issue(reinterpret_cast<const u32x4_t*>(afrag) + (int64_t)a * nbp * 64, nbp * 64);
     const float* sp = spart + (int64_t)a * nbp * 32;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, corr = acc;
-    // ring depth: kRing chunks, 6 for the 16-chunk q4 case (register budget)
-    constexpr int R = NC < kRing ? NC : (FMT == 1 && NC > 8 ? 6 : kRing);
+    // ring depth: kRing chunks, 4 for the 16-chunk case (register budget)
+    constexpr int R = NC < kRing ? NC : (NC > 8 ? 4 : kRing);
     uint32_t cw[R][CWN];
     u32x2_t sc[R];
-    float s0[NC], s1[NC];
-    // block sums of the fragment rows first (small, from L2), then a ring of R
-    // chunks with unconditional (clamped) loads, fully unrolled over NC
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int bq = min(c, md.nch - 1) * 4 + gs;
-        s0[c] = sp[bq * 32 + m];
-        s1[c] = sp[bq * 32 + 16 + m];
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    float s0[R], s1[R];
+    // ring of R chunks (codes, scales and the block sums of the fragment rows)
+    // with unconditional (clamped) loads, fully unrolled over NC
     auto load = [&](int c, int i) {
         const int cc = min(c, md.nch - 1);
         const int64_t off = (int64_t)cc * md.chunk_bytes;
+        const int bq = cc * 4 + gs;
+        s0[i] = sp[bq * 32 + m];
+        s1[i] = sp[bq * 32 + 16 + m];
         load_codes<FMT>(Dt + off, lane, cw[i]);
         sc[i] = load_scales(Dt + off, QF<FMT>::kCW, n);
     };
@@ -619,7 +615,7 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots
 #pragma unroll
         for (int j = 0; j < 4; ++j) A[j] = frag[min(c * 4 + j, nbp - 1) * 64 + lane];
         const u32x2_t scc = c < md.nch ? sc[i] : u32x2_t{0u, 0u};  // padding chunk (NC > nch): zero scales
-        chunk_mac<FMT>(cw[i], scc, A, s0[c] + s1[c], gs, acc, corr);
+        chunk_mac<FMT>(cw[i], scc, A, s0[i] + s1[i], gs, acc, corr);
     };
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -630,10 +626,19 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots
     __syncthreads();
     // waves past the last row tile compute on tile 0 and discard the result:
     // no branch around the refill loads
+    if constexpr (NC <= 8) {
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-        compute(i, i % R);
-        if (i + R < NC) load(i + R, i % R);
+        for (int i = 0; i < NC; ++i) {
+            compute(i, i % R);
+            if (i + R < NC) load(i + R, i % R);
+        }
+    } else {
+        // long K (16 chunks): guarded steps keep the register footprint of one chunk
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            if (i < md.nch) compute(i, i % R);
+            if (i + R < NC && i + R < md.nch) load(i + R, i % R);
+        }
     }
     if (!live) return;
     f32x4_t v;
