@@ -12,7 +12,8 @@ weights and the 256 MB Infinity Cache does not serve repeated reads.
 
 Other workloads (--workload): C3 (the 48-layer chain with residual adds at
 window 1/4/8) and C4 (the 43-layer DeepSeek-shaped chain, 256+1 experts,
-q4b32); a step is then one full chain pass.  C5 is the DeepSeek-shaped
+q4b32); a step is then one full chain pass, with the per-token RMS pre-norm
+of every layer input (without it the stream of random experts overflows).  C5 is the DeepSeek-shaped
 prefill chunk (4096 tokens x hidden 4096, 256+1 experts, top-6, FF 2048,
 q4b32, Zipf-skewed routing): a step is one moe_forward of the whole chunk,
 and the roofline is that of the gate/up grouped GEMM on bf16 MFMA.
@@ -92,7 +93,7 @@ def main():
 
     def step(i, profile=False, trace_ids=None):
         if chain:
-            return ctx.forward(xs[i % len(xs)], 0, L, residual=True, y=y, profile=profile)
+            return ctx.forward(xs[i % len(xs)], 0, L, residual=True, y=y, profile=profile, prenorm=True)
         layer = i % L
         from quantized_expert_ffn_softmax_amd import moe_forward, MOE_FWD_PROFILE
         moe_forward(ctx.handle, xs[i % len(xs)], y, T, layer, 1, MOE_FWD_PROFILE if profile else 0,
@@ -121,7 +122,7 @@ def main():
     U = {}
     for i in range(n_steps_acct):
         if chain:
-            _, _, tid, _ = ctx.forward(xs[i % len(xs)], 0, L, residual=True, trace=True)
+            _, _, tid, _ = ctx.forward(xs[i % len(xs)], 0, L, residual=True, trace=True, prenorm=True)
             for layer in range(L):
                 U[(layer, i % len(xs))] = len(np.unique(tid[layer].cpu().numpy()))
         else:
@@ -358,7 +359,8 @@ def cpu_baseline(cfg, args, L, chain, T):
         for layer in range(L):
             W, b, ex = mi.layer_inputs(cfg, args.seed, layer)
             t1 = time.perf_counter()
-            y, *_ = oracle.moe_layer(x, cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, cfg.fmt, W, b, ex, cfg.expert_bytes)
+            y, *_ = oracle.moe_layer(oracle.rmsnorm_bf16(x), cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, cfg.fmt, W, b, ex,
+                                     cfg.expert_bytes)
             x = oracle.residual_bf16(x, y)
             t_layers += time.perf_counter() - t1
             calls += 1

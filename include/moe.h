@@ -106,12 +106,17 @@ typedef struct {
 
 #define MOE_FWD_RESIDUAL 1 /* x_{l+1} = bf16(fp32(x_l) + y_l); else x_{l+1} = bf16(y_l) */
 #define MOE_FWD_PROFILE 2  /* time every kernel with a HIP event pair bound to its dispatch (moe_profile_read) */
+#define MOE_FWD_PRENORM 4  /* each layer's MoE input is h_l = bf16(x_l / sqrt(mean(x_l^2) + 1e-6)) per token,
+                              fp32 arithmetic, unit gain; the residual still adds to x_l.  The pages' models
+                              normalise every block input; an MoE-only chain of random experts without it
+                              grows without bound and overflows bf16 within a few tens of layers. */
 
 /* One forward pass through layers [layer_begin, layer_begin + layer_count).
  *   x      : [T x H] bf16, device, input of the first layer
  *   y      : [T x H] bf16, device, output of the last layer (the residual
  *            sum when MOE_FWD_RESIDUAL is set); may not alias x
- *   trace_x  : NULL or [layer_count x T x H] bf16, each layer's input
+ *   trace_x  : NULL or [layer_count x T x H] bf16, each layer's MoE input (x_l,
+ *              or h_l when MOE_FWD_PRENORM is set)
  *   trace_ids: NULL or [layer_count x T x k] int32, each layer's routing
  *   trace_w  : NULL or [layer_count x T x k] fp32, each layer's weights */
 typedef struct {
@@ -179,7 +184,8 @@ typedef enum {
     MOE_K_PF_SORT = 7,      /* prefill counting sort (three launches: histogram, scan, scatter) */
     MOE_K_PF_GEMM1 = 8,     /* prefill grouped GEMM gate/up + SwiGLU */
     MOE_K_PF_GEMM2 = 9,     /* prefill grouped GEMM down */
-    MOE_K_PF_COMBINE = 10   /* prefill weighted combine */
+    MOE_K_PF_COMBINE = 10,  /* prefill weighted combine */
+    MOE_K_NORM = 11         /* per-token RMS pre-norm (MOE_FWD_PRENORM) */
 } moe_kernel_kind;
 
 typedef struct {

@@ -62,6 +62,8 @@ def lib():
         L.oracle_moe_layer.restype = None
         L.oracle_residual_bf16.argtypes = [ctypes.c_uint16, f64]
         L.oracle_residual_bf16.restype = ctypes.c_uint16
+        L.oracle_rmsnorm_bf16.argtypes = [vp, i32, f64, vp]
+        L.oracle_rmsnorm_bf16.restype = None
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = i32
         _lib = L
@@ -183,6 +185,18 @@ def residual_bf16(x_bits: np.ndarray, y: np.ndarray) -> np.ndarray:
     xb = np.asarray(x_bits, dtype=np.uint16).ravel()
     yv = np.asarray(y, dtype=np.float64).ravel()
     out = np.array([f(int(a), float(b)) for a, b in zip(xb, yv)], dtype=np.uint16)
+    return out.reshape(np.shape(x_bits))
+
+
+RMSNORM_EPS = 1e-6
+
+
+def rmsnorm_bf16(x_bits: np.ndarray, eps: float = RMSNORM_EPS) -> np.ndarray:
+    """Per-token unit-gain RMS normalisation, rounded once to bf16 (rows of x)."""
+    x = np.ascontiguousarray(np.atleast_2d(x_bits), dtype=np.uint16)
+    out = np.empty_like(x)
+    for t in range(x.shape[0]):
+        lib().oracle_rmsnorm_bf16(_p(x[t]), x.shape[1], eps, _p(out[t]))
     return out.reshape(np.shape(x_bits))
 
 

@@ -266,6 +266,51 @@ uint16_t oracle_residual_bf16(uint16_t x, double y) {
     return (uint16_t)(u >> 16);
 }
 
+/* Pre-norm of a layer chain: unit-gain RMS normalisation of one token's
+ * hidden state, h_i = bf16_rne(x_i / sqrt(mean_j x_j^2 + eps)), in fp64 with a
+ * single rounding to bf16.  The MoE-only chains keep each layer's input at
+ * the unit scale the activations are drawn at (the pages' models normalise
+ * the input of every block; without it the residual stream of random experts
+ * grows without bound and overflows bf16 within a few tens of layers). */
+void oracle_rmsnorm_bf16(const uint16_t* x, int n, double eps, uint16_t* h) {
+    double ss = 0.0;
+    for (int i = 0; i < n; ++i) {
+        const double v = oracle_bf16(x[i]);
+        ss += v * v;
+    }
+    const double r = 1.0 / sqrt(ss / n + eps);
+    for (int i = 0; i < n; ++i) {
+        const double v = oracle_bf16(x[i]) * r;
+        /* round the double to bf16, nearest-even, from its exact binary64 bits */
+        uint64_t u;
+        memcpy(&u, &v, 8);
+        const uint64_t sign = u >> 63;
+        const int e = (int)((u >> 52) & 0x7FF);
+        uint16_t out;
+        if (e == 0x7FF) {
+            out = (uint16_t)((sign << 15) | 0x7F80u | ((u & 0xFFFFFFFFFFFFFull) ? 0x40u : 0u));
+        } else {
+            /* value = m * 2^(e - 1075) with m = 2^52 | mantissa; bf16 keeps 8 significant bits */
+            const double a = fabs(v);
+            int ex;
+            const double fr = frexp(a, &ex);             /* a = fr * 2^ex, fr in [0.5, 1) */
+            double q = ldexp(fr, 8);                      /* 8 significant bits in the integer part */
+            if (ex - 8 < -133) q = ldexp(a, 133);         /* subnormal bf16: fixed quantum 2^-133 */
+            const double fl = floor(q);
+            const double rem = q - fl;
+            double rq = fl;
+            if (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0)) rq = fl + 1.0;
+            const double rv = ex - 8 < -133 ? ldexp(rq, -133) : ldexp(rq, ex - 8);
+            const float f = (float)rv;                    /* exact: rv has at most 8 significant bits */
+            uint32_t fu;
+            memcpy(&fu, &f, 4);
+            out = (uint16_t)((fu >> 16) | (sign << 15));
+            (void)e;
+        }
+        h[i] = out;
+    }
+}
+
 /* Number of OpenMP threads the oracle's parallel loops use. */
 int oracle_num_threads(void) {
     int n = 1;

@@ -21,8 +21,9 @@ MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_ESTATE, MOE_ERANGE = 0, -1, -2, -3
 MOE_Q4B32, MOE_Q2B32 = 1, 2
 MOE_FWD_RESIDUAL = 1
 MOE_FWD_PROFILE = 2
+MOE_FWD_PRENORM = 4
 KERNEL_NAMES = {0: "router", 1: "topk_sort", 2: "gateup", 3: "down", 4: "combine", 5: "pf_router", 6: "pf_topk",
-                7: "pf_sort", 8: "pf_gemm1", 9: "pf_gemm2", 10: "pf_combine"}
+                7: "pf_sort", 8: "pf_gemm1", 9: "pf_gemm2", 10: "pf_combine", 11: "norm"}
 MOE_ABI_VERSION = 1
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOMEM", -3: "MOE_EHIP", -4: "MOE_ESTATE", -5: "MOE_ERANGE"}
 
@@ -197,7 +198,7 @@ class MoEContext:
         return ids, w, offsets, perm
 
     def forward(self, x, layer_begin=0, layer_count=1, residual=False, trace=False, y=None, stream=None,
-                profile=False):
+                profile=False, prenorm=False):
         import torch
         T = x.shape[0]
         if y is None:
@@ -207,7 +208,8 @@ class MoEContext:
             tx = torch.empty((layer_count, T, self.H), dtype=x.dtype, device=x.device)
             tid = torch.empty((layer_count, T, self.k), dtype=torch.int32, device=x.device)
             tw = torch.empty((layer_count, T, self.k), dtype=torch.float32, device=x.device)
-        flags = (MOE_FWD_RESIDUAL if residual else 0) | (MOE_FWD_PROFILE if profile else 0)
+        flags = ((MOE_FWD_RESIDUAL if residual else 0) | (MOE_FWD_PROFILE if profile else 0) |
+                 (MOE_FWD_PRENORM if prenorm else 0))
         moe_forward(self.handle, x, y, T, layer_begin, layer_count, flags, tx, tid, tw, stream)
         return (y, tx, tid, tw) if trace else y
 

@@ -63,6 +63,7 @@ struct moe_ctx {
     bool prefill = false;          // max_tokens > kMaxDecodeT: prefill scratch present
     float* rstat = nullptr;        // L x 2: max router row norm, max |bias| (prefill candidate bound)
     uint16_t* xbuf[2] = {nullptr, nullptr};
+    uint16_t* hbuf = nullptr;      // [max_tokens x H] normalised MoE input (MOE_FWD_PRENORM)
     int maxA = 0;
     int decode_T = 0;
     // upload
@@ -188,6 +189,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     const size_t o_part = cv.take<float>((size_t)c->maxA * kMaxDecodeT * g.H);
     const size_t o_x0 = cv.take<uint16_t>((size_t)Tm * g.H);
     const size_t o_x1 = cv.take<uint16_t>((size_t)Tm * g.H);
+    const size_t o_h = cv.take<uint16_t>((size_t)Tm * g.H);
     c->prefill = cfg->max_tokens > kMaxDecodeT;
     size_t p_logits = 0, p_ids = 0, p_w = 0, p_blkcnt = 0, p_rank = 0, p_off = 0, p_perm = 0, p_inv = 0, p_rowtok = 0,
            p_blkbase = 0, p_tiles = 0, p_ntiles = 0, p_h = 0, p_o = 0;
@@ -252,6 +254,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     c->db.part = (float*)(b + o_part);
     c->xbuf[0] = (uint16_t*)(b + o_x0);
     c->xbuf[1] = (uint16_t*)(b + o_x1);
+    c->hbuf = (uint16_t*)(b + o_h);
     if (c->prefill) {
         c->pb.logits = (float*)(b + p_logits);
         c->pb.ids = (int32_t*)(b + p_ids);
@@ -464,7 +467,8 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
         return fail(MOE_EINVAL, "layers [%d, %d) outside [0, %d)", a->layer_begin, a->layer_begin + a->layer_count, g.L);
     if (a->T < 0) return fail(MOE_EINVAL, "T %d is negative", a->T);
     if (a->T > c->cfg.max_tokens) return fail(MOE_ERANGE, "T %d above max_tokens %d", a->T, c->cfg.max_tokens);
-    if (a->flags & ~(MOE_FWD_RESIDUAL | MOE_FWD_PROFILE)) return fail(MOE_EINVAL, "unknown flags 0x%x", a->flags);
+    if (a->flags & ~(MOE_FWD_RESIDUAL | MOE_FWD_PROFILE | MOE_FWD_PRENORM))
+        return fail(MOE_EINVAL, "unknown flags 0x%x", a->flags);
     if (a->T == 0) return MOE_OK;
     if (!a->x || !a->y) return fail(MOE_EINVAL, "x and y are required");
     if (!aligned16(a->x) || !aligned16(a->y) || (a->trace_x && !aligned16(a->trace_x)))
@@ -485,17 +489,26 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
         const int l = a->layer_begin + i;
         const bool last = i == a->layer_count - 1;
         uint16_t* yout = last ? (uint16_t*)a->y : c->xbuf[i & 1];
-        if (a->trace_x)
-            HIP_TRY(c, hipMemcpyAsync((uint8_t*)a->trace_x + (size_t)i * xbytes, xin, xbytes, hipMemcpyDeviceToDevice, st));
         const bool prof = (a->flags & MOE_FWD_PROFILE) != 0;
+        // xm: the MoE input of this layer (the normalised stream with MOE_FWD_PRENORM); the residual adds to xin
+        const uint16_t* xm = xin;
+        if (a->flags & MOE_FWD_PRENORM) {
+            moe_status s = timed(c, prof, MOE_K_NORM, l, st,
+                                 [&](const Launch& lc) { return launch_rmsnorm(xin, T, g.H, c->hbuf, lc); },
+                                 "pre-norm kernel launch");
+            if (s != MOE_OK) return s;
+            xm = c->hbuf;
+        }
+        if (a->trace_x)
+            HIP_TRY(c, hipMemcpyAsync((uint8_t*)a->trace_x + (size_t)i * xbytes, xm, xbytes, hipMemcpyDeviceToDevice, st));
         const uint8_t* slots = c->arena + (size_t)l * ES * g.slot_bytes;
         int32_t* tids = a->trace_ids ? a->trace_ids + (size_t)i * T * g.k : nullptr;
         float* tw = a->trace_w ? a->trace_w + (size_t)i * T * g.k : nullptr;
         if (pf) {
-            moe_status s = route_prefill(c, l, xin, T, tids, tw, st, prof);
+            moe_status s = route_prefill(c, l, xm, T, tids, tw, st, prof);
             if (s != MOE_OK) return s;
             s = timed(c, prof, MOE_K_PF_GEMM1, l, st,
-                      [&](const Launch& lc) { return launch_pf_gemm1(xin, slots, g, c->pb, lc); },
+                      [&](const Launch& lc) { return launch_pf_gemm1(xm, slots, g, c->pb, lc); },
                       "prefill gate/up GEMM launch");
             if (s != MOE_OK) return s;
             s = timed(c, prof, MOE_K_PF_GEMM2, l, st,
@@ -508,10 +521,10 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
             xin = yout;
             continue;
         }
-        moe_status s = route_decode(c, l, xin, T, tids, tw, st, prof);
+        moe_status s = route_decode(c, l, xm, T, tids, tw, st, prof);
         if (s != MOE_OK) return s;
         s = timed(c, prof, MOE_K_GATEUP, l, st,
-                  [&](const Launch& lc) { return launch_gateup_decode(xin, T, slots, g, c->rb, c->db, c->maxA, lc); },
+                  [&](const Launch& lc) { return launch_gateup_decode(xm, T, slots, g, c->rb, c->db, c->maxA, lc); },
                   "gate/up kernel launch");
         if (s != MOE_OK) return s;
         s = timed(c, prof, MOE_K_DOWN, l, st,

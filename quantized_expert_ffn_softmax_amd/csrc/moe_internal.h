@@ -152,6 +152,10 @@ hipError_t launch_down_decode(int T, const uint8_t* layer_slots, const Geom& g, 
 hipError_t launch_combine_decode(const uint16_t* x, int T, const Geom& g, RouteBufs rb, DecodeBufs db, uint16_t* y,
                                  int residual, const Launch& lc);
 
+// Per-token unit-gain RMS normalisation h = bf16(x / sqrt(mean(x^2) + eps)), fp32.
+constexpr float kNormEps = 1e-6f;
+hipError_t launch_rmsnorm(const uint16_t* x, int T, int H, uint16_t* h, const Launch& lc);
+
 // Prefill launchers; rstat = {max_e ||W_r[e]||_2, max_e |b[e]|} of the layer's router.
 hipError_t launch_router_stats(const uint16_t* Wr, const float* bias, int E, int H, float* rstat, hipStream_t st);
 hipError_t launch_pf_router(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const Geom& g,

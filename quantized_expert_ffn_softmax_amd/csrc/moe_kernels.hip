@@ -693,6 +693,47 @@ hipError_t launch_down_decode(int T, const uint8_t* layer_slots, const Geom& g, 
 #undef MOE_DOWN_CASE
 }
 
+// ---------------------------------------------------------------- pre-norm
+// One workgroup per token: sum of squares in fp32 (each thread strides over
+// 16-byte groups, then a fixed wave/LDS tree), then h = bf16(x * 1/sqrt(ms + eps)).
+__global__ __launch_bounds__(256) void k_rmsnorm(const uint16_t* __restrict__ x, int H, uint16_t* __restrict__ h) {
+    __shared__ float s_part[4];
+    const int t = blockIdx.x;
+    const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (int64_t)t * H);
+    u32x4_t* hr = reinterpret_cast<u32x4_t*>(h + (int64_t)t * H);
+    const int n16 = H / 8;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < n16; i += blockDim.x) {
+        const u32x4_t v = xr[i];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float a = bf2f(v[q] & 0xFFFFu), b = bf2f(v[q] >> 16);
+            ss = fmaf(a, a, ss);
+            ss = fmaf(b, b, ss);
+        }
+    }
+    ss = row_sum_f32(ss);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+    const float r = 1.0f / sqrtf(tot / (float)H + kNormEps);
+    for (int i = threadIdx.x; i < n16; i += blockDim.x) {
+        const u32x4_t v = xr[i];
+        u32x4_t o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            o[q] = f2bf(bf2f(v[q] & 0xFFFFu) * r) | (f2bf(bf2f(v[q] >> 16) * r) << 16);
+        hr[i] = o;
+    }
+}
+
+hipError_t launch_rmsnorm(const uint16_t* x, int T, int H, uint16_t* h, const Launch& lc) {
+    launch(k_rmsnorm, dim3(T), dim3(256), 0, lc, x, H, h);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- combine
 // y[t][h] = bf16( sum_{a < nact} part[a][t][h]  (+ x[t][h]) ), experts added in
 // ascending active order (routed experts by id, then the shared expert).

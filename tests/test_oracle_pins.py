@@ -284,6 +284,40 @@ def test_residual_rounding_matches_torch():
     np.testing.assert_array_equal(got, ref)
 
 
+# --------------------------------------------------------- chain pre-norm
+def _bits(vals):
+    return (np.asarray(vals, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_rmsnorm_closed_forms():
+    # constant rows normalise to 1 (eps = 0), a (3, 4) row to (3, 4) / sqrt(12.5)
+    np.testing.assert_array_equal(oracle.rmsnorm_bf16(_bits([2.0] * 8), eps=0.0), _bits([1.0] * 8))
+    got = oracle.bf16_to_f64(oracle.rmsnorm_bf16(_bits([3.0, 4.0]), eps=0.0))
+    want = np.array([3.0, 4.0]) / np.sqrt(12.5)
+    assert np.all(np.abs(got - want) <= np.abs(want) * 2.0**-9)
+    # one element of 64 at 1, the rest 0: rms = 1/8, so the element becomes 8
+    row = np.zeros(64, dtype=np.float32)
+    row[5] = 1.0
+    h = oracle.bf16_to_f64(oracle.rmsnorm_bf16(_bits(row), eps=0.0))
+    assert h[5] == 8.0 and np.count_nonzero(h) == 1
+
+
+def test_rmsnorm_matches_torch_rne_and_invariants():
+    xb = mi.gen_x(3, 0, 4, 512)
+    xf = oracle.bf16_to_f64(xb)
+    h = oracle.rmsnorm_bf16(xb)
+    r = xf / np.sqrt((xf**2).mean(axis=1, keepdims=True) + oracle.RMSNORM_EPS)
+    ref = torch.from_numpy(r).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(h, ref)
+    hf = oracle.bf16_to_f64(h)
+    assert np.all(np.abs(np.sqrt((hf**2).mean(axis=1)) - 1.0) < 2.0**-8)
+    # exact invariants with eps = 0: a power-of-two scale drops out, the sign flips through
+    h0 = oracle.rmsnorm_bf16(xb, eps=0.0)
+    x8 = _bits(xf * 8.0)
+    np.testing.assert_array_equal(oracle.rmsnorm_bf16(x8, eps=0.0), h0)
+    np.testing.assert_array_equal(oracle.rmsnorm_bf16(xb ^ np.uint16(0x8000), eps=0.0), h0 ^ np.uint16(0x8000))
+
+
 # --------------------------------------------------------- byte accounting
 def test_byte_accounting_matches_pages():
     # DeepSeek-V4-Flash: the Q4_K expert tensors total 145.125 GiB; q4b32 is the
