@@ -55,11 +55,19 @@ def parse():
     p.add_argument("--seed", type=int, default=1)
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU-baseline leg")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                   help="after the timed work, copy an MB-sized device buffer 8 times (a known-size stream for "
+                        "calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    p.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "MB"),
+                   help="no GPU: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a run made with "
+                        "--copy-calibration MB into profiles/gateup_traffic.json")
     return p.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        return summarize_pmc(args)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported (no collectives)"}))
         sys.exit(2)
@@ -171,6 +179,16 @@ def main():
     kernels_us = {k: round(1e3 * float(np.mean(v)), 2) for k, v in per_kernel.items()}
     log(f"[bench] per-kernel mean us (events): {kernels_us}")
     log(f"[bench] gate/up {gu_achieved:.0f} GB/s, down {dn_achieved:.0f} GB/s, layer {hbm_gbps:.0f} GB/s")
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "gateup_traffic.json")
@@ -325,6 +343,49 @@ def run_prefill(args):
                                   "seconds": round(dt, 2)}
     ctx.close()
     print(json.dumps(result), flush=True)
+
+
+def summarize_pmc(args):
+    """HBM traffic of the gate/up kernel from two counter runs of the same command.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what the
+    same counter reads for the calibration copy (the 8 largest copy dispatches,
+    MB read and MB written each)."""
+    import csv
+    fetch_csv, write_csv, mb = args.summarize_pmc
+    calib_kib = int(mb) * 1024
+
+    def load(path, counter):
+        per = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                per.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        gu = [v for k, vs in per.items() if "k_gateup_decode" in k for v in vs]
+        cp = sorted((v for k, vs in per.items() if "copyBuffer" in k for v in vs), reverse=True)[:8]
+        if not gu or len(cp) < 8:
+            raise SystemExit(f"{path}: {len(gu)} gate/up and {len(cp)} calibration dispatches found")
+        return float(np.mean(gu)), float(np.mean(cp)), len(gu)
+
+    f_gu, f_cp, n_f = load(fetch_csv, "FETCH_SIZE")
+    w_gu, w_cp, n_w = load(write_csv, "WRITE_SIZE")
+    kf, kw = calib_kib / f_cp, calib_kib / w_cp
+    out = {
+        "workload": "C2",
+        "kernel": "k_gateup_decode",
+        "kernel_sha": kernel_sha(),
+        "fetch_kib_per_dispatch": round(f_gu, 1), "write_kib_per_dispatch": round(w_gu, 1),
+        "dispatches": [n_f, n_w],
+        "calibration_copy_MiB": int(mb),
+        "calibration_fetch_kib": round(f_cp, 1), "calibration_write_kib": round(w_cp, 1),
+        "scale_fetch": round(kf, 4), "scale_write": round(kw, 4),
+        "bytes_per_launch": round((f_gu * kf + w_gu * kw) * 1024, 1),
+    }
+    path = os.path.join(ROOT, "profiles", "gateup_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def kernel_sha():
