@@ -4,7 +4,8 @@
 //   k_router_decode   router GEMV (+bias) with fp64 accumulation of the exact
 //                     bf16 x bf16 products; also the per-block sums of x
 //   k_topk_sort       one workgroup: top-k per token (logit descending, lower
-//                     id on ties; DPP wave arg-max), renormalised softmax
+//                     id on ties; DPP wave maxima over pre-sorted per-lane
+//                     lists of 64-bit keys), renormalised softmax
 //                     weights, stable counting sort of the (token, expert)
 //                     pairs from per-expert token bitmasks, active-expert list
 //                     and weight table
@@ -232,7 +233,9 @@ hipError_t launch_router_decode(const uint16_t* x, int T, const uint16_t* Wr, co
 }
 
 // ---------------------------------------------------------------- top-k + sort
-// One workgroup of 4 waves; wave w routes tokens w and w+4.  The counting
+// One workgroup of 4 waves; wave w routes tokens w and w+4 (selection on
+// fp32-rounded keys with an exact fp64 fallback at fp32 ties, see
+// wave_topk_fast; weights from the fp64 logits).  The counting
 // sort uses one bitmask of tokens per expert: the pairs of a token have
 // distinct experts, so the rank of pair (t, j) inside the group of expert e is
 // the number of tokens t' < t that chose e, and the group size is popc(mask).
@@ -247,6 +250,7 @@ __global__ __launch_bounds__(256) void k_topk_sort(int T, int E, int k, int S, R
     __shared__ float s_wtab[(kMaxDecodeT * kMaxTopK + 1) * kMaxDecodeT];
     __shared__ uint32_t s_wsum[4];
     __shared__ int s_U;
+    __shared__ double s_lg[4][64 * J];  // a wave's logits of its current token
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int P = T * k;
     // logits of this wave's tokens (t = wave, wave + 4) are requested first
@@ -266,28 +270,39 @@ __global__ __launch_bounds__(256) void k_topk_sort(int T, int E, int k, int S, R
     for (int r2 = 0; r2 < 2; ++r2) {
         const int t = wave + 4 * r2;
         if (t >= T) break;
-        uint64_t key[J];
-        uint32_t taken = 0;
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            key[j] = lane + 64 * j < E ? order_key(raw[r2][j]) : 0ull;
-            if (lane + 64 * j >= E) taken |= 1u << j;
-        }
-        uint64_t my_k = 0, k0 = 0;
         int my_e = 0;
-        for (int r = 0; r < k; ++r) {
-            uint64_t bk = 0;
-            int be = 0x7FFFFFFF;
+        double my_l = 0.0;
+        if (wave_topk_fast<J>(raw[r2], E, k, lane, my_e)) {
+            // the exact fp64 logits of the selected experts, from this wave's copy in LDS
 #pragma unroll
-            for (int j = 0; j < J; ++j)
-                if (!((taken >> j) & 1u) && ahead(key[j], lane + 64 * j, bk, be)) { bk = key[j]; be = lane + 64 * j; }
-            wave_argmax(bk, be);
-            if ((be & 63) == lane) taken |= 1u << (be >> 6);
-            if (r == 0) k0 = bk;
-            if (lane == r) { my_k = bk; my_e = be; }
+            for (int j = 0; j < J; ++j) s_lg[wave][lane + 64 * j] = raw[r2][j];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            my_l = s_lg[wave][my_e];
+        } else {
+            // fp32 ties among the k+1 best: select on the fp64 logits, (logit, id) order
+            uint64_t key[J];
+            uint32_t taken = 0;
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                key[j] = lane + 64 * j < E ? order_key(raw[r2][j]) : 0ull;
+                if (lane + 64 * j >= E) taken |= 1u << j;
+            }
+            for (int r = 0; r < k; ++r) {
+                uint64_t bk = 0;
+                int be = 0x7FFFFFFF;
+#pragma unroll
+                for (int j = 0; j < J; ++j)
+                    if (!((taken >> j) & 1u) && ahead(key[j], lane + 64 * j, bk, be)) { bk = key[j]; be = lane + 64 * j; }
+                wave_argmax(bk, be);
+                if ((be & 63) == lane) taken |= 1u << (be >> 6);
+                if (lane == r) { my_l = key_value(bk); my_e = be; }
+            }
         }
+        const double l0 = __shfl(my_l, 0);
         // renormalised softmax over the selected logits (fp64)
-        const double ex = lane < k ? exp(key_value(my_k) - key_value(k0)) : 0.0;
+        const double ex = lane < k ? exp(my_l - l0) : 0.0;
         const double z = wave_sum_f64(ex);
         if (lane < k) {
             const float wv = (float)(ex / z);
