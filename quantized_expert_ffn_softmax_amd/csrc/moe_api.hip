@@ -508,7 +508,7 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
             moe_status s = route_prefill(c, l, xm, T, tids, tw, st, prof);
             if (s != MOE_OK) return s;
             s = timed(c, prof, MOE_K_PF_GEMM1, l, st,
-                      [&](const Launch& lc) { return launch_pf_gemm1(xm, slots, g, c->pb, lc); },
+                      [&](const Launch& lc) { return launch_pf_gemm1(xm, T, slots, g, c->pb, lc); },
                       "prefill gate/up GEMM launch");
             if (s != MOE_OK) return s;
             s = timed(c, prof, MOE_K_PF_GEMM2, l, st,

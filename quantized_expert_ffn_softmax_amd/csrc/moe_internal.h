@@ -126,6 +126,7 @@ struct PrefillBufs {
     uint16_t* h;       // [(T*k + S*T) x F] bf16 SwiGLU output in sorted row order
     float* o;          // [(T*k + S*T) x H] fp32 per-row expert outputs
     int max_tiles;
+    int T;             // tokens of the current call (set by the GEMM launchers on their copy)
 };
 inline int prefill_max_tiles(int T, int k, int E, int S) {
     const int64_t P = (int64_t)T * k;
@@ -165,7 +166,7 @@ hipError_t launch_pf_topk(const uint16_t* x, int T, const uint16_t* Wr, const fl
 hipError_t launch_pf_hist(int T, const Geom& g, PrefillBufs pb, const Launch& lc);
 hipError_t launch_pf_scan(int T, const Geom& g, PrefillBufs pb, const Launch& lc);
 hipError_t launch_pf_scatter(int T, const Geom& g, PrefillBufs pb, const Launch& lc);
-hipError_t launch_pf_gemm1(const uint16_t* x, const uint8_t* layer_slots, const Geom& g, PrefillBufs pb,
+hipError_t launch_pf_gemm1(const uint16_t* x, int T, const uint8_t* layer_slots, const Geom& g, PrefillBufs pb,
                            const Launch& lc);
 hipError_t launch_pf_gemm2(const uint8_t* layer_slots, const Geom& g, PrefillBufs pb, const Launch& lc);
 hipError_t launch_pf_combine(const uint16_t* x, int T, const Geom& g, PrefillBufs pb, uint16_t* y, int residual,

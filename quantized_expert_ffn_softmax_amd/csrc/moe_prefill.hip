@@ -382,23 +382,29 @@ __global__ __launch_bounds__(256) void k_pf_scatter(int T, int E, int k, int S, 
 }
 
 // ---------------------------------------------------------------- grouped GEMMs
-constexpr int kLdsRow = 136;                // bf16 per LDS row: 128 + 8 (rows 272 bytes apart: b128 reads conflict-free)
-constexpr int kLdsTile = 128 * kLdsRow;     // one activation tile (elements)
-constexpr int kGemmLds = 2 * kLdsTile * 2;  // double buffer, bytes
+// Activation tile of one 128-wide K chunk: 128 rows of 256 bytes, written by
+// direct global->LDS loads.  Slot p of row r holds the row's 16-byte segment
+// p ^ (r % 16), so the b128 fragment reads of 16 consecutive rows at one
+// segment hit 16 distinct bank groups.
+constexpr int kATileBytes = 128 * 256;
+constexpr int kGemmLds = 2 * kATileBytes;  // double buffer
 
-// Work item of block b: V = ntiles * ntn items, item i = (M-block i / ntn,
-// N-tile i % ntn).  Workgroups are dealt to the 8 XCDs round-robin (b % 8), so
-// XCD x is given the contiguous item range [x V/8, (x+1) V/8) (remainder to
-// the first XCDs): all N-tiles of an M-block share one XCD's L2.
+// Work item of block b.  Workgroups are dealt to the 8 XCDs round-robin, so
+// block b runs on XCD x = b % 8 as its slot s = b / 8 there.  M-blocks are
+// dealt to the XCDs round-robin too (the i-th M-block of XCD x is list entry
+// x + 8 i, counted from the end of the list), and slot s holds N-tile s % ntn
+// of that XCD's M-block s / ntn: the N-tiles of an M-block run one after the
+// other on one XCD (its activation tile is fetched into that L2 once), and
+// large and small groups spread evenly over the XCDs.  The list ends with
+// the shared expert's full blocks, so walking it backwards starts each XCD
+// on the longest items.  The grid holds 8 ceil(ntiles / 8) ntn blocks.
 __device__ __forceinline__ bool pf_item(int ntn, int ntiles, int& m, int& n) {
-    const int V = ntiles * ntn;
-    const int b = blockIdx.x;
-    if (b >= V) return false;
-    const int xcd = b & 7, s = b >> 3;
-    const int q = V >> 3, r = V & 7;
-    const int L = xcd * q + min(xcd, r) + s;
-    m = L / ntn;
-    n = L - m * ntn;
+    const int b = blockIdx.x, x = b & 7, s = b >> 3;
+    const int i = s / ntn;
+    const int mi = x + 8 * i;
+    if (mi >= ntiles) return false;
+    m = ntiles - 1 - mi;
+    n = s - i * ntn;
     return true;
 }
 
@@ -411,17 +417,29 @@ template <int FMT> struct BCodes;
 template <> struct BCodes<1> { u32x4_t c0, c1; u32x2_t sc; };
 template <> struct BCodes<2> { u32x2_t c0, c1; u32x2_t sc; };
 
+// Weight codes and activations are read through buffer resources: the
+// wave-uniform base and the chunk's offset live in scalar registers, the
+// lane's offset is a loop-invariant 32-bit register, so advancing a chunk
+// costs no vector instruction.  dword3 0x00020000: raw 32-bit data.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Codes of one chunk: soff = the chunk's byte offset in the expert slot;
+// offc / offs = the lane's byte offsets of its first code word and of its
+// scales in a chunk.  A row tile past the matrix (N not a multiple of the
+// tile) reads the last one again: the columns it feeds are never stored.
 template <int FMT>
-__device__ __forceinline__ void load_bcodes(BCodes<FMT>& b, const uint8_t* chunk, int n16, int half, bool valid) {
+__device__ __forceinline__ void load_bcodes(BCodes<FMT>& b, __amdgpu_buffer_rsrc_t r, uint32_t soff, uint32_t offc,
+                                            uint32_t offs) {
     if constexpr (FMT == 1) {
-        b.c0 = *reinterpret_cast<const u32x4_t*>(chunk + (n16 + 16 * half) * 16);
-        b.c1 = *reinterpret_cast<const u32x4_t*>(chunk + (n16 + 16 * (half + 2)) * 16);
+        b.c0 = __builtin_amdgcn_raw_buffer_load_b128(r, offc, soff, 0);
+        b.c1 = __builtin_amdgcn_raw_buffer_load_b128(r, offc + 32 * 16, soff, 0);
     } else {
-        b.c0 = *reinterpret_cast<const u32x2_t*>(chunk + (n16 + 16 * half) * 8);
-        b.c1 = *reinterpret_cast<const u32x2_t*>(chunk + (n16 + 16 * (half + 2)) * 8);
+        b.c0 = __builtin_amdgcn_raw_buffer_load_b64(r, offc, soff, 0);
+        b.c1 = __builtin_amdgcn_raw_buffer_load_b64(r, offc + 32 * 8, soff, 0);
     }
-    b.sc = *reinterpret_cast<const u32x2_t*>(chunk + 64 * QF<FMT>::kCW + n16 * 8);
-    if (!valid) b.sc = u32x2_t{0u, 0u};  // row tile past the matrix: zero weights
+    b.sc = __builtin_amdgcn_raw_buffer_load_b64(r, offs, soff, 0);
 }
 
 __device__ __forceinline__ float ub0(uint32_t v) { return (float)(v & 0xFFu); }
@@ -433,18 +451,21 @@ __device__ __forceinline__ float ub3(uint32_t v) { return (float)(v >> 24); }
 // (11 + 4 significant bits) and -o*d is exact (o a power of two), so the fma
 // is the exact weight; the pack rounds it once to bf16.
 // q4 word: nibble p (bits 4p) = element 2p, nibble p+4 (bits 16+4p) = element 2p+1.
-__device__ __forceinline__ u32x4_t deq_q4(uint32_t w, float d) {
-    const uint32_t lo = w & 0x0F0F0F0Fu;         // bytes: e0 e4 e1 e5
-    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // bytes: e2 e6 e3 e7
-    const float c = -8.f * d;
+// The two masked words are made opaque to the compiler: it would otherwise
+// extract every nibble from w with its own v_bfe, where one v_cvt_f32_ubyteN
+// of a masked word does the extraction and the conversion at once.
+// c = -o d, exact (o a power of two), passed in like d as an fp16 value.
+__device__ __forceinline__ u32x4_t deq_q4(uint32_t w, float d, float c) {
+    uint32_t lo = w & 0x0F0F0F0Fu;         // bytes: e0 e4 e1 e5
+    uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // bytes: e2 e6 e3 e7
+    asm("" : "+v"(lo), "+v"(hi));
     return u32x4_t{pack_bf16(fmaf(d, ub0(lo), c), fmaf(d, ub2(lo), c)),
                    pack_bf16(fmaf(d, ub0(hi), c), fmaf(d, ub2(hi), c)),
                    pack_bf16(fmaf(d, ub1(lo), c), fmaf(d, ub3(lo), c)),
                    pack_bf16(fmaf(d, ub1(hi), c), fmaf(d, ub3(hi), c))};
 }
 // q2 (block bits already at 0..7 and 16..23): bits 2p = element 2p, bits 16+2p = element 2p+1.
-__device__ __forceinline__ u32x4_t deq_q2(uint32_t w, float d) {
-    const float c = -2.f * d;
+__device__ __forceinline__ u32x4_t deq_q2(uint32_t w, float d, float c) {
     u32x4_t r;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -453,16 +474,200 @@ __device__ __forceinline__ u32x4_t deq_q2(uint32_t w, float d) {
     }
     return r;
 }
-// B operands of block j: K steps 2j (lo) and 2j+1 (hi).
+// B operand of K step ks (block ks / 2: lo half for even ks, hi half for odd);
+// a dead chunk (live false) gets zero scales.
+// sc: the row's four fp16 block scales (zeroed for a dead chunk).  d and
+// c = -o d (exact: o is a power of two) enter the fma as fp16 operands,
+// converted exactly by v_fma_mix_f32; c costs one v_mul_f16 per block.
+// (Written with scalar halves: the same product over bit-cast f16x2 words
+// has been compiled to reuse the first word's products for the second.)
+__device__ __forceinline__ _Float16 scale_h(u32x2_t s, int j) {
+    const uint32_t w = (j & 2) ? s.y : s.x;
+    return __builtin_bit_cast(_Float16, (uint16_t)((j & 1) ? (w >> 16) : (w & 0xFFFFu)));
+}
 template <int FMT>
-__device__ __forceinline__ void deq_block(const BCodes<FMT>& b, int j, u32x4_t& lo, u32x4_t& hi) {
-    const float d = scale_of(b.sc, j);
+__device__ __forceinline__ u32x4_t deq_half(const BCodes<FMT>& b, int ks, u32x2_t sc) {
+    const int j = ks >> 1;
+    const _Float16 dh = scale_h(sc, j);
+    const _Float16 ch = dh * (_Float16)(FMT == 1 ? -8.f : -2.f);
+    const float d = (float)dh, c = (float)ch;
     if constexpr (FMT == 1) {
-        lo = deq_q4(b.c0[j], d);
-        hi = deq_q4(b.c1[j], d);
+        return deq_q4((ks & 1) ? b.c1[j] : b.c0[j], d, c);
     } else {
-        lo = deq_q2(b.c0[j >> 1] >> (8 * (j & 1)), d);
-        hi = deq_q2(b.c1[j >> 1] >> (8 * (j & 1)), d);
+        return deq_q2(((ks & 1) ? b.c1[j >> 1] : b.c0[j >> 1]) >> (8 * (j & 1)), d, c);
+    }
+}
+
+// Per-thread state of one GEMM work item, shared by the slice-count
+// specialisations of the main loop.
+// Every load address is a wave-uniform base plus a 32-bit lane offset, so the
+// loads take the scalar-base form and the per-chunk address math is scalar.
+struct GemmItem {
+    __amdgpu_buffer_rsrc_t ar;  // activation rows (x, or the M-block's rows of h)
+    __amdgpu_buffer_rsrc_t br;  // the group's expert slot
+    uint32_t aoff[8];           // byte offsets of this lane's 8 A segments in chunk 0 (rows past nrows repeat the last)
+    uint32_t boffc[2];          // per 32-column group: byte offset of this lane's code words in chunk 0
+    uint32_t boffs[2];          // ... and of its row's scales
+    int row0, nrows, nt, wave, nk, K;
+    uint32_t chunk_bytes;
+};
+
+// Main loop and epilogue for NS 32-row slices.  Every slice of the item holds
+// at least one row, so the loop body is branch-free: per 32-wide K block the
+// wave dequantises the four B operands it needs, reads the 2 NS activation
+// fragments, and issues 4 NS MFMAs.  Chunk kc + 1 (activations by DMA into the
+// other LDS buffer, weight codes into registers) is requested before chunk kc
+// is computed.
+template <int FMT, int MODE, int NS>
+__device__ __forceinline__ void gemm_item(GemmItem& it, uint8_t* As, const Geom& g, const PrefillBufs& pb) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int n = lane & 31, half = lane >> 5;
+    // wave w loads the rows of slice w: instruction q covers rows 32w + 4q .. +3,
+    // lane l writes slot l % 16 of row 32w + 4q + l / 16.  A segment past K
+    // is replaced by the row's last one (its weights are zero).  The loads are
+    // issued without branches (the waits of a load under a branch are placed
+    // at the join), so waves past the last slice load rows no one reads.
+    auto load_a = [&](int kc, int buf) {
+        uint8_t* dst = As + buf * kATileBytes + it.wave * 8192;
+        const uint32_t soff = (uint32_t)kc * 256;
+        if (kc * 128 + 128 <= it.K) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(it.ar, (__attribute__((address_space(3))) void*)(dst + q * 1024),
+                                                         16, it.aoff[q], soff, 0, 0);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int e = kc * 128 + 8 * ((lane & 15) ^ ((4 * q + (lane >> 4)) & 15));
+                const uint32_t over = (uint32_t)max(e - (it.K - 8), 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(it.ar, (__attribute__((address_space(3))) void*)(dst + q * 1024),
+                                                         16, it.aoff[q] - 2 * over, soff, 0, 0);
+            }
+        }
+    };
+    f32x16_t acc[NS][2];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[s][gi][i] = 0.f;
+
+    // weight codes of even chunks in bc0, odd chunks in bc1 (no copies between chunks)
+    BCodes<FMT> bc0[2], bc1[2];
+    load_a(0, 0);
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) load_bcodes<FMT>(bc0[gi], it.br, 0u, it.boffc[gi], it.boffs[gi]);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
+    __syncthreads();
+    // LDS byte offset of this lane's fragment row (slice 0) and its segment swizzle
+    const uint8_t* al0 = As + (lane & 31) * 256;
+    const int swz = lane & 15;
+    // chunk kc >= nk (the partner of the last chunk when nk is odd) repeats the
+    // last chunk's data with zero scales: it adds exact zeros
+    auto chunk = [&](int kc, int buf, const BCodes<FMT>(&cb)[2], BCodes<FMT>(&nb)[2]) {
+        const bool live = kc < it.nk;
+        const int kn = min(kc + 1, it.nk - 1);  // past the end: the last chunk again
+        load_a(kn, buf ^ 1);
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+            load_bcodes<FMT>(nb[gi], it.br, (uint32_t)kn * it.chunk_bytes, it.boffc[gi], it.boffs[gi]);
+        // the next chunk is requested before this chunk's work (the scheduler
+        // would otherwise sink the loads to their use)
+        __builtin_amdgcn_sched_barrier(0);
+        const uint8_t* al = al0 + buf * kATileBytes;
+        // 16-wide K steps (block ks / 2, half ks % 2), software-pipelined: the
+        // activation fragments and the dequantised weights of step ks + 1 are
+        // prepared while the MFMAs of step ks run
+        auto read_a = [&](int ks, u32x4_t (&af)[NS]) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                af[s] = *reinterpret_cast<const u32x4_t*>(al + s * 8192 + (((2 * ks + half) ^ swz) << 4));
+        };
+        u32x2_t sc[2];
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) sc[gi] = live ? cb[gi].sc : u32x2_t{0u, 0u};
+        u32x4_t afc[NS], b0c, b1c;
+        read_a(0, afc);
+        b0c = deq_half<FMT>(cb[0], 0, sc[0]);
+        b1c = deq_half<FMT>(cb[1], 0, sc[1]);
+        // issue order of this region: step 0's reads and dequantisation, then
+        // per step the next step's reads followed by its MFMAs, each MFMA
+        // followed by a share of the next step's dequantisation
+        __builtin_amdgcn_sched_group_barrier(0x100, NS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 56, 0);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            u32x4_t afn[NS], b0n, b1n;
+            if (ks < 7) {
+                read_a(ks + 1, afn);
+                b0n = deq_half<FMT>(cb[0], ks + 1, sc[0]);
+                b1n = deq_half<FMT>(cb[1], ks + 1, sc[1]);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                acc[s][0] = mfma32(afc[s], b0c, acc[s][0]);
+                acc[s][1] = mfma32(afc[s], b1c, acc[s][1]);
+            }
+            if (ks < 7) {
+#pragma unroll
+                for (int s = 0; s < NS; ++s) afc[s] = afn[s];
+                b0c = b0n;
+                b1c = b1n;
+                __builtin_amdgcn_sched_group_barrier(0x100, NS, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 2 * NS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, (56 + 2 * NS - 1) / (2 * NS), 0);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): chunk kc + 1 has landed
+        __syncthreads();
+    };
+    // pairs of chunks without a branch between them: a load whose only use
+    // sits under a branch is moved there by the compiler, past the barrier
+    for (int kc = 0; kc < it.nk; kc += 2) {
+        chunk(kc, 0, bc0, bc1);
+        chunk(kc + 1, 1, bc1, bc0);
+    }
+    // epilogue: lane holds C[m = 32 s + 8(i/4) + 4 half + i%4][column n] of both groups
+    if constexpr (MODE == 1) {
+        // SwiGLU -> bf16 tile [row][128 features] in LDS (the activation
+        // buffers are idle after the last barrier), then 16-byte row stores
+        uint16_t* hl = reinterpret_cast<uint16_t*>(As);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = s * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                const float gv = acc[s][0][i], uv = acc[s][1][i];
+                hl[m * 128 + 32 * it.wave + n] = (uint16_t)f2bf(gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv);
+            }
+        __syncthreads();
+        const int nfe = min(128, g.F - it.nt * 128);  // features of this tile (a multiple of 32)
+#pragma unroll
+        for (int q = 0; q < 2 * NS; ++q) {
+            const int idx = tid + 256 * q, r = idx >> 4, c8 = (idx & 15) * 8;
+            if (r < it.nrows && c8 < nfe)
+                *reinterpret_cast<u32x4_t*>(pb.h + (int64_t)(it.row0 + r) * g.F + it.nt * 128 + c8) =
+                    *reinterpret_cast<const u32x4_t*>(hl + r * 128 + c8);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = s * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                if (m < it.nrows) {
+#pragma unroll
+                    for (int gi = 0; gi < 2; ++gi) {
+                        const int col = it.nt * 256 + 64 * it.wave + 32 * gi + n;
+                        if (col < g.H) pb.o[(int64_t)(it.row0 + m) * g.H + col] = acc[s][gi][i];
+                    }
+                }
+            }
+        }
     }
 }
 
@@ -470,138 +675,66 @@ __device__ __forceinline__ void deq_block(const BCodes<FMT>& b, int j, u32x4_t& 
 // rows; epilogue SwiGLU -> h.  MODE 2: A = h rows, K = F; groups = two
 // consecutive 32-row stripes of D; epilogue -> o.
 template <int FMT, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_pf_gemm(const uint16_t* __restrict__ x, const uint8_t* __restrict__ slots,
-                                                 Geom g, PrefillBufs pb, int ntn) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_pf_gemm(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ slots, Geom g, PrefillBufs pb, int ntn) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     int mt, nt;
     if (!pf_item(ntn, pb.ntiles[0], mt, nt)) return;
     const int* tl = pb.tiles + 4 * mt;
-    const int row0 = tl[0], nrows = tl[1], grp = tl[2];
+    GemmItem it;
+    it.row0 = tl[0];
+    it.nrows = tl[1];
+    const int grp = tl[2];
+    it.nt = nt;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nslice = (nrows + 31) >> 5;
-    uint16_t* As = reinterpret_cast<uint16_t*>(smem);
-    const int K = MODE == 1 ? g.H : g.F;
+    it.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nslice = (it.nrows + 31) >> 5;
+    it.K = MODE == 1 ? g.H : g.F;
     const MatGeom& mg = MODE == 1 ? g.gu : g.dn;
-    const int nk = mg.nch;
-    const uint8_t* slot = slots + (int64_t)grp * g.slot_bytes;
-    // B: this lane's row tiles of the two groups
+    it.nk = mg.nch;
+    it.chunk_bytes = (uint32_t)mg.chunk_bytes;
+    it.br = make_rsrc(slots + (int64_t)grp * g.slot_bytes, (uint32_t)g.slot_bytes);
     const int n = lane & 31, half = lane >> 5;
-    const uint8_t* bt[2];
-    bool bvalid[2];
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
         int rt;
-        const uint8_t* base;
+        uint32_t base;
         if constexpr (MODE == 1) {
-            rt = nt * 8 + 2 * wave + (n >> 4);
-            base = slot + (gi ? g.u_off : g.g_off);
+            rt = nt * 8 + 2 * it.wave + (n >> 4);
+            base = (uint32_t)(gi ? g.u_off : g.g_off);
         } else {
-            rt = nt * 16 + 4 * wave + 2 * gi + (n >> 4);
-            base = slot + g.d_off;
+            rt = nt * 16 + 4 * it.wave + 2 * gi + (n >> 4);
+            base = (uint32_t)g.d_off;
         }
-        bvalid[gi] = rt < mg.rows / 16;
-        bt[gi] = base + (int64_t)min(rt, mg.rows / 16 - 1) * mg.tile_bytes;
+        // lane l takes the slot-lanes (n % 16, half) and (n % 16, half + 2) of its row tile
+        const uint32_t tile = base + (uint32_t)min(rt, mg.rows / 16 - 1) * (uint32_t)mg.tile_bytes;
+        it.boffc[gi] = tile + (uint32_t)((n & 15) + 16 * half) * QF<FMT>::kCW;
+        it.boffs[gi] = tile + 64 * QF<FMT>::kCW + (uint32_t)(n & 15) * 8;
     }
-    // A: 128 rows x 16 segments of 16 bytes per chunk, 8 per thread (rows past nrows repeat the last)
-    const uint16_t* abase = MODE == 1 ? x : pb.h;
-    uint32_t aoff[8];  // element offsets (< 2^32: T*H and (T*k + T)*F are bounded by the context limits)
+    // A: lane l of instruction q of wave w fetches segment (l % 16) ^ (r % 16)
+    // of tile row r = 32 w + 4 q + l / 16
+    // (MODE 2: the M-block's rows are contiguous in h; its first row goes into
+    // the base, so the lane offsets stay below 128 F 2 bytes)
+    if constexpr (MODE == 1)
+        it.ar = make_rsrc(x, (uint32_t)(pb.T * g.H * 2));
+    else
+        it.ar = make_rsrc(pb.h + (int64_t)it.row0 * g.F, (uint32_t)(it.nrows * g.F * 2));
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        const int i = tid + 256 * q;
-        const int r = min(i >> 4, nrows - 1);
+        const int r = 32 * it.wave + 4 * q + (lane >> 4);
+        const int rr = min(r, it.nrows - 1);
+        const uint32_t seg = (uint32_t)((lane & 15) ^ (r & 15));
         if constexpr (MODE == 1)
-            aoff[q] = (uint32_t)pb.rowtok[row0 + r] * (uint32_t)g.H + 8 * (i & 15);
+            it.aoff[q] = 2 * ((uint32_t)pb.rowtok[it.row0 + rr] * (uint32_t)g.H + 8 * seg);
         else
-            aoff[q] = (uint32_t)(row0 + r) * (uint32_t)g.F + 8 * (i & 15);
+            it.aoff[q] = 2 * ((uint32_t)rr * (uint32_t)g.F + 8 * seg);
     }
-    u32x4_t av[8];
-    auto load_a = [&](int kc) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int kk = kc * 128 + 8 * ((tid + 256 * q) & 15);
-            av[q] = u32x4_t{0u, 0u, 0u, 0u};
-            if (kk < K) av[q] = *reinterpret_cast<const u32x4_t*>(abase + (aoff[q] + kc * 128));
-        }
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int i = tid + 256 * q;
-            *reinterpret_cast<u32x4_t*>(As + buf * kLdsTile + (i >> 4) * kLdsRow + 8 * (i & 15)) = av[q];
-        }
-    };
-    BCodes<FMT> cb[2], nb[2];
-    f32x16_t acc[4][2];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[s][gi][i] = 0.f;
-
-    load_a(0);
-#pragma unroll
-    for (int gi = 0; gi < 2; ++gi) load_bcodes<FMT>(cb[gi], bt[gi], n & 15, half, bvalid[gi]);
-    store_a(0);
-    if (nk > 1) load_a(1);
-    __syncthreads();
-    for (int kc = 0; kc < nk; ++kc) {
-        const int buf = kc & 1;
-        const int kn = min(kc + 1, nk - 1);
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
-            load_bcodes<FMT>(nb[gi], bt[gi] + (int64_t)kn * mg.chunk_bytes, n & 15, half, bvalid[gi]);
-        const uint16_t* al = As + buf * kLdsTile + (lane & 31) * kLdsRow + 8 * half;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            u32x4_t b0[2], b1[2];
-            deq_block<FMT>(cb[0], j, b0[0], b0[1]);
-            deq_block<FMT>(cb[1], j, b1[0], b1[1]);
-#pragma unroll
-            for (int ss = 0; ss < 2; ++ss) {
-                const int ks = 2 * j + ss;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    if (s < nslice) {
-                        const u32x4_t af = *reinterpret_cast<const u32x4_t*>(al + s * 32 * kLdsRow + 16 * ks);
-                        acc[s][0] = mfma32(af, b0[ss], acc[s][0]);
-                        acc[s][1] = mfma32(af, b1[ss], acc[s][1]);
-                    }
-                }
-            }
-        }
-        if (kc + 1 < nk) store_a(buf ^ 1);
-        if (kc + 2 < nk) load_a(kc + 2);
-        __syncthreads();
-        cb[0] = nb[0];
-        cb[1] = nb[1];
-    }
-    // epilogue: lane holds C[m = 32 s + 8(i/4) + 4 half + i%4][column n] of both groups
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        if (s < nslice) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int m = s * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                if (m < nrows) {
-                    if constexpr (MODE == 1) {
-                        const int f = nt * 128 + 32 * wave + n;
-                        if (f < g.F) {
-                            const float gv = acc[s][0][i], uv = acc[s][1][i];
-                            const float hv = gv / (1.0f + __expf(-gv)) * uv;
-                            pb.h[(int64_t)(row0 + m) * g.F + f] = (uint16_t)f2bf(hv);
-                        }
-                    } else {
-#pragma unroll
-                        for (int gi = 0; gi < 2; ++gi) {
-                            const int col = nt * 256 + 64 * wave + 32 * gi + n;
-                            if (col < g.H) pb.o[(int64_t)(row0 + m) * g.H + col] = acc[s][gi][i];
-                        }
-                    }
-                }
-            }
-        }
+    uint8_t* As = smem;
+    switch (nslice) {
+        case 1: gemm_item<FMT, MODE, 1>(it, As, g, pb); break;
+        case 2: gemm_item<FMT, MODE, 2>(it, As, g, pb); break;
+        case 3: gemm_item<FMT, MODE, 3>(it, As, g, pb); break;
+        default: gemm_item<FMT, MODE, 4>(it, As, g, pb); break;
     }
 }
 
@@ -691,12 +824,13 @@ static hipError_t launch_gemm(const uint16_t* x, const uint8_t* slots, const Geo
     hipError_t e = ensure_lds(k_pf_gemm<FMT, MODE>, kGemmLds, granted);
     if (e != hipSuccess) return e;
     const int ntn = MODE == 1 ? (g.F + 127) / 128 : (g.H + 255) / 256;
-    launch(k_pf_gemm<FMT, MODE>, dim3(pb.max_tiles * ntn), dim3(256), kGemmLds, lc, x, slots, g, pb, ntn);
+    launch(k_pf_gemm<FMT, MODE>, dim3(((pb.max_tiles + 7) & ~7) * ntn), dim3(256), kGemmLds, lc, x, slots, g, pb, ntn);
     return hipGetLastError();
 }
 
-hipError_t launch_pf_gemm1(const uint16_t* x, const uint8_t* layer_slots, const Geom& g, PrefillBufs pb,
+hipError_t launch_pf_gemm1(const uint16_t* x, int T, const uint8_t* layer_slots, const Geom& g, PrefillBufs pb,
                            const Launch& lc) {
+    pb.T = T;
     return g.fmt == 1 ? launch_gemm<1, 1>(x, layer_slots, g, pb, lc) : launch_gemm<2, 1>(x, layer_slots, g, pb, lc);
 }
 
