@@ -26,8 +26,9 @@
 // GEMM workgroup: 4 waves, an M-block of up to 128 sorted rows (32-row
 // slices; only slices holding rows run MFMAs) by 256 output columns; wave w
 // owns 64 columns as two 32-column groups.  The activation tile of each
-// 128-wide K chunk is gathered into double-buffered LDS (rows padded to 272
-// bytes, conflict-free b128 reads); the weights never touch LDS: every wave
+// 128-wide K chunk is gathered by buffer DMA into double-buffered LDS (256-byte
+// rows, segments XOR-swizzled by row: conflict-free b128 reads); the weights
+// never touch LDS: every wave
 // loads the codes of its own columns in the slot layout and dequantises them
 // in registers straight into MFMA B operands, w = d*(q - o) computed exactly
 // in fp32 and rounded once to bf16.  Work items are mapped XCD-aware: the
