@@ -127,46 +127,42 @@ hipError_t launch_repack(const uint8_t* canon, uint8_t* slots, int count, const 
 }
 
 // ---------------------------------------------------------------- router
-// Grid ceil(E/4) workgroups of 4 waves; wave w of workgroup b computes the
-// logits of expert 4b+w for every token.  Every bf16 x bf16 product is exact
-// in fp32 and is accumulated in fp64 (fixed reduction tree), so the selection
-// agrees with an fp64 evaluation except at logit gaps near 1e-15.
-// The workgroup first requests its share of x (into registers), then every
-// wave requests its whole router row (up to 8 x 16 bytes per lane, H <= 4096);
-// x is written to LDS once it has arrived, while the row loads are still in
-// flight, and the math waits for each row load on its own.
+// Grid E workgroups of 4 waves; workgroup e computes the logits of expert e
+// for every token.  Wave w sums the quarter h in [w H/4, (w+1) H/4): every
+// bf16 x bf16 product is exact in fp32 and is accumulated in fp64; the four
+// quarter sums are added in a fixed order, so the selection agrees with an
+// fp64 evaluation except at logit gaps near 1e-15.  A lane owns NJ 16-byte
+// segments of its quarter (NJ = ceil(H / 2048)) and requests the router
+// row's segments and the TT token rows' segments (TT = T rounded up to a power
+// of two; rows past T repeat the last) all at once, before any math.
 // All threads of the grid also share the per-block sums
 // sx[b][m] = sum_{q<32} x[m][32b+q] (fp32, in q order; zero for m >= T).
-constexpr int kRouterPass = 8;  // 16-byte loads per lane: H <= 4096
-
-template <int XPER>
+template <int NJ, int TT>
 __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restrict__ x, int T,
                                                        const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
                                                        int E, int H, int nbp, double* __restrict__ logits,
                                                        float* __restrict__ sx) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [T][H]
+    __shared__ double s_part[4][TT];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int e = blockIdx.x * 4 + wave;
-    const uint16_t* wrow = Wr + (int64_t)(e < E ? e : E - 1) * H;
-    const int n16 = T * (H / 8);
-    StageRegs<XPER> xst;
-    xst.issue(reinterpret_cast<const u32x4_t*>(x), n16);
-    u32x4_t wv[kRouterPass];
+    const int e = blockIdx.x;
+    const int ns = H / 32;  // 16-byte segments per quarter
+    const int h0 = wave * (H / 4);
+    u32x4_t wv[NJ], xv[NJ][TT];
 #pragma unroll
-    for (int j = 0; j < kRouterPass; ++j) wv[j] = *reinterpret_cast<const u32x4_t*>(wrow + min((lane + 64 * j) * 8, H - 8));
-    __builtin_amdgcn_sched_barrier(0);
-    const double be = bias ? (double)bias[e < E ? e : E - 1] : 0.0;
-    xst.commit(reinterpret_cast<u32x4_t*>(xs), n16, [](int i) { return i; }, n16);
-    __syncthreads();
-    double acc[kMaxDecodeT];
+    for (int j = 0; j < NJ; ++j) {
+        const int seg = min(lane + 64 * j, ns - 1);
+        wv[j] = *reinterpret_cast<const u32x4_t*>(Wr + (int64_t)e * H + h0 + 8 * seg);
 #pragma unroll
-    for (int t = 0; t < kMaxDecodeT; ++t) acc[t] = 0.0;
+        for (int t = 0; t < TT; ++t)
+            xv[j][t] = *reinterpret_cast<const u32x4_t*>(x + (int64_t)min(t, T - 1) * H + h0 + 8 * seg);
+    }
+    double acc[TT];
 #pragma unroll
-    for (int j = 0; j < kRouterPass; ++j) {
-        const int h0 = (lane + 64 * j) * 8;
-        if (h0 < H) {
+    for (int t = 0; t < TT; ++t) acc[t] = 0.0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        if (lane + 64 * j < ns) {
             float wf[8];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -174,31 +170,32 @@ __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restric
                 wf[2 * q + 1] = __uint_as_float(wv[j][q] & 0xFFFF0000u);
             }
 #pragma unroll
-            for (int t = 0; t < kMaxDecodeT; ++t) {
-                if (t < T) {
-                    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs + t * H + h0);
+            for (int t = 0; t < TT; ++t) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[t] += (double)(__uint_as_float(xv[q] << 16) * wf[2 * q]);
-                        acc[t] += (double)(__uint_as_float(xv[q] & 0xFFFF0000u) * wf[2 * q + 1]);
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    acc[t] += (double)(__uint_as_float(xv[j][t][q] << 16) * wf[2 * q]);
+                    acc[t] += (double)(__uint_as_float(xv[j][t][q] & 0xFFFF0000u) * wf[2 * q + 1]);
                 }
             }
         }
     }
 #pragma unroll
-    for (int t = 0; t < kMaxDecodeT; ++t) {
-        if (t < T) {
-            const double v = wave_sum_f64(acc[t]);
-            if (lane == 0 && e < E) logits[(int64_t)t * E + e] = v + be;
-        }
+    for (int t = 0; t < TT; ++t) {
+        const double v = wave_sum_f64(acc[t]);
+        if (lane == 0) s_part[wave][t] = v;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < T) {
+        const int t = threadIdx.x;
+        const double be = bias ? (double)bias[e] : 0.0;
+        logits[(int64_t)t * E + e] = ((s_part[0][t] + s_part[1][t]) + (s_part[2][t] + s_part[3][t])) + be;
     }
     const int nb = H / 32;
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nbp * 16; i += gridDim.x * blockDim.x) {
         const int b = i >> 4, m = i & 15;
         float s = 0.f;
         if (m < T && b < nb) {
-            const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(xs + m * H + b * 32);
+            const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (int64_t)m * H + b * 32);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const u32x4_t v = xr[r];
@@ -215,19 +212,16 @@ __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restric
 
 hipError_t launch_router_decode(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const Geom& g,
                                 RouteBufs rb, const Launch& lc) {
-    const int lds = T * g.H * 2 + 16;  // + the dummy slot of the staging stores
-    const int per = (T * (g.H / 8) + 255) / 256;  // <= 16 (T <= 8, H <= 4096)
-    const dim3 grid((g.E + 3) / 4);
-    hipError_t e;
-#define MOE_ROUTER_CASE(P)                                                                                       \
-    if (per <= P) {                                                                                              \
-        static int granted = 64 * 1024;                                                                          \
-        if ((e = ensure_lds(k_router_decode<P>, lds, granted)) != hipSuccess) return e;                          \
-        launch(k_router_decode<P>, grid, dim3(256), lds, lc, x, T, Wr, bias, g.E, g.H, g.gu.nch * 4, rb.logits,  \
-               rb.sx);                                                                                           \
-        return hipGetLastError();                                                                                \
+    const dim3 grid(g.E);
+    const int nj = (g.H / 32 + 63) / 64;  // 1 or 2 (H <= 4096)
+#define MOE_ROUTER_CASE(NJ, TT)                                                                                    \
+    if (nj == NJ && T <= TT) {                                                                                     \
+        launch(k_router_decode<NJ, TT>, grid, dim3(256), 0, lc, x, T, Wr, bias, g.E, g.H, g.gu.nch * 4, rb.logits, \
+               rb.sx);                                                                                             \
+        return hipGetLastError();                                                                                  \
     }
-    MOE_ROUTER_CASE(2) MOE_ROUTER_CASE(4) MOE_ROUTER_CASE(8) MOE_ROUTER_CASE(16)
+    MOE_ROUTER_CASE(1, 1) MOE_ROUTER_CASE(1, 2) MOE_ROUTER_CASE(1, 4) MOE_ROUTER_CASE(1, 8)
+    MOE_ROUTER_CASE(2, 1) MOE_ROUTER_CASE(2, 2) MOE_ROUTER_CASE(2, 4) MOE_ROUTER_CASE(2, 8)
 #undef MOE_ROUTER_CASE
     return hipErrorInvalidValue;
 }
