@@ -169,74 +169,68 @@ __device__ __forceinline__ void wave_argmax(uint64_t& k, int& e) {
     k = ((uint64_t)hi << 32) | lo;
 }
 
-// Wave-wide maximum of a 64-bit key (DPP butterflies within rows, row
+// Wave-wide maximum of a 32-bit key (DPP butterflies within rows, row
 // broadcasts into lane 63, read back as a wave-uniform value).
-template <int CTRL> __device__ __forceinline__ void max_step_u64(uint64_t& k) {
-    const uint32_t lo = (uint32_t)dpp<CTRL>((int)(uint32_t)k);
-    const uint32_t hi = (uint32_t)dpp<CTRL>((int)(uint32_t)(k >> 32));
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
+template <int CTRL> __device__ __forceinline__ void max_step_u32(uint32_t& k) {
+    const uint32_t o = (uint32_t)dpp<CTRL>((int)k);
     k = o > k ? o : k;
 }
-template <int CTRL, int ROWS> __device__ __forceinline__ void max_bcast_u64(uint64_t& k) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)k, (int)(uint32_t)k, CTRL, ROWS, 0xF, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(k >> 32), (int)(uint32_t)(k >> 32), CTRL,
-                                                              ROWS, 0xF, false);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
+template <int CTRL, int ROWS> __device__ __forceinline__ void max_bcast_u32(uint32_t& k) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)k, (int)k, CTRL, ROWS, 0xF, false);
     k = o > k ? o : k;
 }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-    max_step_u64<kDppXor1>(k);
-    max_step_u64<kDppXor2>(k);
-    max_step_u64<kDppHalfMirror>(k);
-    max_step_u64<kDppMirror>(k);
-    max_bcast_u64<0x142, 0xA>(k);
-    max_bcast_u64<0x143, 0xC>(k);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 63);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t k) {
+    max_step_u32<kDppXor1>(k);
+    max_step_u32<kDppXor2>(k);
+    max_step_u32<kDppHalfMirror>(k);
+    max_step_u32<kDppMirror>(k);
+    max_bcast_u32<0x142, 0xA>(k);
+    max_bcast_u32<0x143, 0xC>(k);
+    return (uint32_t)__builtin_amdgcn_readlane((int)k, 63);
 }
 
 // Top-k of the logits a wave holds (lane l, slot j: expert l + 64 j, valid
-// below E), selected on fp32-rounded values with the expert id folded into one
-// 64-bit key (value descending, then id ascending), so every comparison is a
-// single 64-bit compare.  Each lane sorts its J keys once; a round takes the
-// wave maximum of the lanes' heads and the winning lane drops its head.
-// Rounding to fp32 is monotone, so if the k+1 best fp32 values are pairwise
-// distinct the order equals the fp64 order; otherwise (near or exact ties) the
+// below E <= 1024), selected on one 32-bit key per expert: the order-preserving
+// image of the fp32-rounded logit with its low 10 bits replaced by 1023 - e
+// (value descending, then id ascending), so every comparison is one unsigned
+// compare.  Each lane sorts its J keys once; a round takes the wave maximum of
+// the lanes' heads and the winning lane drops its head.  Rounding to fp32 and
+// dropping 10 low bits are both monotone: if the k+1 best keys differ above
+// bit 10, their order is the fp64 order; otherwise (near or exact ties) the
 // function returns false and the caller selects on the fp64 values.  On
 // success lane r < k holds the id of rank r in my_e.
 template <int J>
 __device__ __forceinline__ bool wave_topk_fast(const double* raw, int E, int k, int lane, int& my_e) {
-    uint64_t key[J];
+    uint32_t key[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int e = lane + 64 * j;
         const uint32_t u = __float_as_uint((float)raw[j] + 0.0f);
         const uint32_t kf = (u >> 31) ? ~u : (u | 0x80000000u);
-        key[j] = e < E ? ((uint64_t)kf << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e) : 0ull;
+        key[j] = e < E ? (kf & ~0x3FFu) | (uint32_t)(1023 - e) : 0u;
     }
 #pragma unroll
     for (int i = 1; i < J; ++i)
 #pragma unroll
         for (int j = i; j > 0; --j) {
-            const uint64_t a = key[j - 1], b = key[j];
+            const uint32_t a = key[j - 1], b = key[j];
             key[j - 1] = a > b ? a : b;
             key[j] = a > b ? b : a;
         }
-    uint64_t mine = 0;
+    uint32_t mine = 0;
     for (int r = 0; r <= k; ++r) {
-        const uint64_t best = wave_max_u64(key[0]);
+        const uint32_t best = wave_max_u32(key[0]);
         // the winning lane drops its head: a bitwise select (v_bfi_b32), not an indexed move
-        const uint64_t m = key[0] == best ? ~0ull : 0ull;
+        const uint32_t m = key[0] == best ? ~0u : 0u;
 #pragma unroll
         for (int j = 0; j + 1 < J; ++j) key[j] = (key[j + 1] & m) | (key[j] & ~m);
         key[J - 1] &= ~m;
         mine = lane == r ? best : mine;
     }
-    const uint32_t hv = (uint32_t)(mine >> 32);
+    const uint32_t hv = mine >> 10;
     const uint32_t hn = (uint32_t)__shfl_down((int)hv, 1);
-    if (__ballot(lane < k && (mine == 0ull || hv == hn))) return false;
-    my_e = lane < k ? (int)(0xFFFFFFFFu - (uint32_t)mine) : 0;
+    if (__ballot(lane < k && (mine == 0u || hv == hn))) return false;
+    my_e = lane < k ? 1023 - (int)(mine & 0x3FFu) : 0;
     return true;
 }
 

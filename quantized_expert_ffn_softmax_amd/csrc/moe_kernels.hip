@@ -1,11 +1,12 @@
 // Decode-path kernels of the MI355X sparse-MoE layer (gfx950, wave64).
 //
 // Per layer and call (T <= 8 tokens), five launches:
-//   k_router_decode   router GEMV (+bias) with fp64 accumulation of the exact
-//                     bf16 x bf16 products; also the per-block sums of x
+//   k_router_decode   one workgroup per expert: router GEMV (+bias) with fp64
+//                     accumulation of the exact bf16 x bf16 products; also
+//                     the per-block sums of x
 //   k_topk_sort       one workgroup: top-k per token (logit descending, lower
 //                     id on ties; DPP wave maxima over pre-sorted per-lane
-//                     lists of 64-bit keys), renormalised softmax
+//                     lists of 32-bit keys), renormalised softmax
 //                     weights, stable counting sort of the (token, expert)
 //                     pairs from per-expert token bitmasks, active-expert list
 //                     and weight table
@@ -228,7 +229,8 @@ hipError_t launch_router_decode(const uint16_t* x, int T, const uint16_t* Wr, co
 
 // ---------------------------------------------------------------- top-k + sort
 // One workgroup of 4 waves; wave w routes tokens w and w+4 (selection on
-// fp32-rounded keys with an exact fp64 fallback at fp32 ties, see
+// 32-bit keys of the fp32-rounded logit and the id, with an exact fp64
+// fallback when two of the k+1 best keys agree above the id bits, see
 // wave_topk_fast; weights from the fp64 logits).  The counting
 // sort uses one bitmask of tokens per expert: the pairs of a token have
 // distinct experts, so the rank of pair (t, j) inside the group of expert e is

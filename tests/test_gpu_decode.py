@@ -126,6 +126,33 @@ def test_tie_break_duplicated_router_rows(torch_cuda):
         assert np.all(w.cpu().numpy() == 0.5)
 
 
+@pytest.mark.parametrize("nudge", [1, -1], ids=["up", "down"])
+def test_near_tie_falls_back_to_exact_order(torch_cuda, nudge):
+    """Experts 3 and 11 differ by one bf16 unit in one router weight and share a
+    large bias: their logits differ by ~1e-4, far below what the fp32 selection
+    keys resolve, so the kernel must select on the fp64 logits.  Ids and their
+    order must equal the oracle's for every token (whichever of the two wins
+    depends on the sign of that token's x element)."""
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    cfg = MoEConfig("near_tie", (8,), 256, 64, 16, 0, 2, 1, Q4B32, mi.BIAS_NONE, 0.0)
+    W = mi.gen_router(6, 0, cfg.E, cfg.H)
+    W[11] = W[3]
+    W[11, 17] = np.uint16(int(W[3, 17]) + nudge)  # one unit in the last place of a bf16 (same sign)
+    bias = np.zeros(cfg.E, dtype=np.float32)
+    bias[3] = bias[11] = 50.0
+    ex = mi.gen_experts(6, 0, 0, cfg.E, cfg.H, cfg.F, cfg.fmt)
+    x = mi.gen_x(6, 0, 8, cfg.H)
+    lg = oracle.router_logits(x, W, bias)
+    assert np.all(lg[:, 3] != lg[:, 11]), "the nudge must separate the two logits"
+    ids_ref, w_ref = oracle.select_topk(lg, cfg.k)
+    with MoEContext.from_config(cfg) as ctx:
+        ctx.load(0, router_w=W, router_bias=bias, experts=ex)
+        ids, w, _, _ = ctx.route(0, to_dev_bf16(x))
+        np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+        assert np.abs(w.cpu().numpy().astype(np.float64) - w_ref).max() <= W_TOL
+        assert set(map(tuple, ids_ref.tolist())) <= {(3, 11), (11, 3)}
+
+
 def test_zero_tokens_and_error_paths(torch_cuda):
     import torch
     from quantized_expert_ffn_softmax_amd import (MOE_EINVAL, MOE_ERANGE, MOE_ESTATE, MoEContext, MoEError,
