@@ -747,7 +747,10 @@ hipError_t launch_rmsnorm(const uint16_t* x, int T, int H, uint16_t* h, const La
 
 // ---------------------------------------------------------------- combine
 // y[t][h] = bf16( sum_{a < nact} part[a][t][h]  (+ x[t][h]) ), experts added in
-// ascending active order (routed experts by id, then the shared expert).
+// ascending active order (routed experts by id, then the shared expert).  The
+// partials are requested 16 at a time (unconditional loads, clamped index;
+// entries past nact are added as zeros), so the sum costs ceil(nact / 16)
+// memory round trips.
 __global__ __launch_bounds__(256) void k_combine_decode(const uint16_t* __restrict__ x, int T, int H,
                                                         const int32_t* __restrict__ nact,
                                                         const float* __restrict__ part, uint16_t* __restrict__ y,
@@ -758,16 +761,13 @@ __global__ __launch_bounds__(256) void k_combine_decode(const uint16_t* __restri
     const float* p = part + i;  // part[a][t][h] with t*H + h = i
     const int64_t stride = (int64_t)kMaxDecodeT * H;
     float s = 0.f;
-    int a = 0;
-    for (; a + 4 <= nA; a += 4) {
-        const float p0 = p[(a + 0) * stride], p1 = p[(a + 1) * stride];
-        const float p2 = p[(a + 2) * stride], p3 = p[(a + 3) * stride];
-        s += p0;
-        s += p1;
-        s += p2;
-        s += p3;
+    for (int a0 = 0; a0 < nA; a0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v[q] = p[min(a0 + q, nA - 1) * stride];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) s += a0 + q < nA ? v[q] : 0.f;
     }
-    for (; a < nA; ++a) s += p[a * stride];
     if (residual) s += bf2f(x[i]);
     y[i] = (uint16_t)f2bf(s);
 }
