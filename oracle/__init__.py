@@ -54,6 +54,8 @@ def lib():
         L.oracle_router_logits.restype = None
         L.oracle_select_topk.argtypes = [vp, i32, i32, i32, vp, vp]
         L.oracle_select_topk.restype = None
+        L.oracle_route_hash.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
+        L.oracle_route_hash.restype = None
         L.oracle_permutation.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
         L.oracle_permutation.restype = None
         L.oracle_combine.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp]
@@ -138,6 +140,22 @@ def select_topk(logits: np.ndarray, k: int):
     ids = np.empty((T, k), dtype=np.int32)
     w = np.empty((T, k), dtype=np.float64)
     lib().oracle_select_topk(_p(logits), T, E, k, _p(ids), _p(w))
+    return ids, w
+
+
+def route_hash(logits: np.ndarray, table: np.ndarray, tok: np.ndarray):
+    """Hash routing: ids[t] = table[tok[t]] (table order), weights = the
+    softmax over all E logits renormalised over those ids."""
+    logits = np.ascontiguousarray(logits, dtype=np.float64)
+    table = np.ascontiguousarray(table, dtype=np.int32)
+    tok = np.ascontiguousarray(tok, dtype=np.int32)
+    T, E = logits.shape
+    k = table.shape[1]
+    assert tok.shape == (T,) and tok.min() >= 0 and tok.max() < table.shape[0]
+    assert table.min() >= 0 and table.max() < E
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float64)
+    lib().oracle_route_hash(_p(logits), T, E, k, _p(table), _p(tok), _p(ids), _p(w))
     return ids, w
 
 

@@ -15,6 +15,8 @@
  *   expert  g = G x, u = U x, a_f = silu(g_f) * u_f, o = D a      (silu(z) = z/(1+e^-z))
  *   combine y_t = sum_j w_tj * o_{t,id_tj}  (+ o_shared with weight 1)
  *   permute a stable counting sort of the pair indices i = t*k + j by expert id
+ *   (hash-routed layers take their experts from a token-id table instead of
+ *   the top-k, see oracle_route_hash)
  *
  * Where the definition comes from:
  *  - Sparse top-k routing over hundreds of experts with a shared expert, and
@@ -174,6 +176,35 @@ void oracle_select_topk(const double* logits, int T, int E, int k, int32_t* ids,
         }
     }
     free(c);
+    free(p);
+}
+
+/* Hash routing, the reading taken for DeepSeek V4 Flash's tid2eid layers
+ * (page "Strata 改源码去跑 DeepSeek V4 Flash？", section 二: layers 0-2 route
+ * by a token-id -> experts table, the other layers by score with a router
+ * bias).  The page gives the table's name and layers only; read here: the
+ * experts of token t are row tok[t] of the [vocab x k] table, in table order,
+ * and their weights are the softmax over all E logits renormalised over those
+ * k experts, the same weight rule as score routing.  The caller guarantees
+ * 0 <= tok[t] < vocab and distinct ids in [0, E) per row. */
+void oracle_route_hash(const double* logits, int T, int E, int k, const int32_t* table, const int32_t* tok,
+                       int32_t* ids, double* w) {
+    double* p = (double*)malloc(sizeof(double) * (size_t)E);
+    for (int t = 0; t < T; ++t) {
+        const double* l = logits + (int64_t)t * E;
+        const int32_t* row = table + (int64_t)tok[t] * k;
+        double m = l[0];
+        for (int e = 1; e < E; ++e) m = l[e] > m ? l[e] : m;
+        double z = 0.0;
+        for (int e = 0; e < E; ++e) { p[e] = exp(l[e] - m); z += p[e]; }
+        for (int e = 0; e < E; ++e) p[e] /= z;
+        double s = 0.0;
+        for (int j = 0; j < k; ++j) s += p[row[j]];
+        for (int j = 0; j < k; ++j) {
+            ids[(int64_t)t * k + j] = row[j];
+            w[(int64_t)t * k + j] = p[row[j]] / s;
+        }
+    }
     free(p);
 }
 

@@ -183,6 +183,59 @@ def test_weights_sum_to_one_and_special_cases():
 
 
 # -------------------------------------------------------------- permutation
+def test_hash_routing_two_experts_is_the_logistic_function():
+    """k = 2: the weights are sigmoid(l_a - l_b) and its complement (scipy)."""
+    rng = np.random.default_rng(11)
+    lg = rng.normal(0, 2, (64, 9))
+    table = np.stack([rng.permutation(9)[:2] for _ in range(20)]).astype(np.int32)
+    tok = rng.integers(0, 20, 64).astype(np.int32)
+    ids, w = oracle.route_hash(lg, table, tok)
+    np.testing.assert_array_equal(ids, table[tok])  # table order, not logit order
+    la = lg[np.arange(64), ids[:, 0]]
+    lb = lg[np.arange(64), ids[:, 1]]
+    np.testing.assert_allclose(w[:, 0], scipy.special.expit(la - lb), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(w[:, 1], scipy.special.expit(lb - la), rtol=0, atol=1e-14)
+
+
+def test_hash_routing_with_the_top_k_table_equals_score_routing():
+    """A table whose row for each token is that token's score top-k gives the
+    score-routing result (ids and weights), so the two weight rules agree."""
+    rng = np.random.default_rng(12)
+    T, E, k = 32, 40, 5
+    lg = rng.normal(0, 1, (T, E))
+    ids_s, w_s = oracle.select_topk(lg, k)
+    ids_h, w_h = oracle.route_hash(lg, ids_s, np.arange(T, dtype=np.int32))
+    np.testing.assert_array_equal(ids_h, ids_s)
+    np.testing.assert_allclose(w_h, w_s, rtol=0, atol=1e-15)
+
+
+def test_hash_routing_invariants():
+    """Weights sum to 1, k = 1 gives exactly 1, a per-token shift of all logits
+    and any change to the logits of experts outside the row leave them
+    unchanged, and permuting a row permutes its weights the same way."""
+    rng = np.random.default_rng(13)
+    T, E, k, V = 24, 30, 4, 50
+    lg = rng.normal(0, 3, (T, E))
+    table = np.stack([rng.permutation(E)[:k] for _ in range(V)]).astype(np.int32)
+    tok = rng.integers(0, V, T).astype(np.int32)
+    ids, w = oracle.route_hash(lg, table, tok)
+    np.testing.assert_allclose(w.sum(1), 1.0, rtol=0, atol=1e-14)
+    _, w1 = oracle.route_hash(lg, table[:, :1].copy(), tok)
+    assert np.all(w1 == 1.0)
+    _, w_shift = oracle.route_hash(lg + rng.normal(0, 5, (T, 1)), table, tok)
+    np.testing.assert_allclose(w_shift, w, rtol=0, atol=1e-13)
+    lg2 = lg.copy()
+    outside = np.ones((T, E), bool)
+    outside[np.arange(T)[:, None], ids] = False
+    lg2[outside] = rng.normal(0, 3, outside.sum())
+    _, w_out = oracle.route_hash(lg2, table, tok)
+    np.testing.assert_allclose(w_out, w, rtol=0, atol=1e-13)
+    perm = rng.permutation(k)
+    ids_p, w_p = oracle.route_hash(lg, table[:, perm].copy(), tok)
+    np.testing.assert_array_equal(ids_p, ids[:, perm])
+    np.testing.assert_allclose(w_p, w[:, perm], rtol=0, atol=1e-15)
+
+
 @pytest.mark.parametrize("T,k,E", [(4, 2, 16), (4, 10, 512), (8, 6, 256), (4096, 6, 256), (1, 1, 1)])
 def test_permutation_matches_stable_argsort(T, k, E):
     rng = np.random.default_rng(T * 1000 + k)
