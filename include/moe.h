@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
     MOE_OK = 0,
@@ -95,13 +95,27 @@ typedef struct {
  *   experts     : expert_count experts in canonical blocks, experts
  *                 [expert_begin, expert_begin + expert_count); index E is the
  *                 shared expert.  NULL with expert_count = 0 uploads none.
- *   experts_bytes must equal expert_count * 3*H*F/32 * (18 or 10). */
+ *   experts_bytes must equal expert_count * 3*H*F/32 * (18 or 10).
+ *   tid2eid     : NULL to leave the layer's routing as is, or a [vocab x k]
+ *                 int32 table (vocab >= 1, ids in [0, E), distinct within a
+ *                 row) that makes the layer hash-routed from this upload on:
+ *                 token t's experts are row token_ids[t] of the table, in
+ *                 table order, and their weights are the softmax of the
+ *                 layer's router logits renormalised over them.  The page
+ *                 "Strata 改源码去跑 DeepSeek V4 Flash？", section 二, lists
+ *                 this routing (tensor tid2eid) for layers 0-2 of DeepSeek
+ *                 V4 Flash and score routing with a router bias for layers
+ *                 3-42; the weight rule is a reading (the page gives none).
+ *                 A hash-routed layer still needs its router uploaded.
+ *   vocab       : rows of tid2eid (ignored when tid2eid is NULL) */
 typedef struct {
     int32_t layer, expert_begin, expert_count;
     const uint16_t* router_w;
     const float* router_bias;
     const uint8_t* experts;
     size_t experts_bytes;
+    const int32_t* tid2eid;
+    int32_t vocab;
 } moe_layer_weights;
 
 #define MOE_FWD_RESIDUAL 1 /* x_{l+1} = bf16(fp32(x_l) + y_l); else x_{l+1} = bf16(y_l) */
@@ -118,7 +132,10 @@ typedef struct {
  *   trace_x  : NULL or [layer_count x T x H] bf16, each layer's MoE input (x_l,
  *              or h_l when MOE_FWD_PRENORM is set)
  *   trace_ids: NULL or [layer_count x T x k] int32, each layer's routing
- *   trace_w  : NULL or [layer_count x T x k] fp32, each layer's weights */
+ *   trace_w  : NULL or [layer_count x T x k] fp32, each layer's weights
+ *   token_ids: NULL or [T] int32, device, 4-byte aligned; required when a
+ *              layer of the range is hash-routed (ids are clamped into
+ *              [0, vocab) on the device) */
 typedef struct {
     int32_t layer_begin, layer_count, T, flags;
     const void* x;
@@ -126,6 +143,7 @@ typedef struct {
     void* trace_x;
     int32_t* trace_ids;
     float* trace_w;
+    const int32_t* token_ids;
 } moe_fwd_args;
 
 typedef struct moe_ctx moe_ctx;
@@ -144,15 +162,19 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out);
 moe_status moe_load_experts(moe_ctx* ctx, const moe_layer_weights* w);
 
 /* Routing of one layer (steps 1-3 above) for T tokens of x [T x H] bf16.
+ *   token_ids : NULL, or [T] int32, device: the tokens' ids, required when the
+ *             layer is hash-routed (see moe_layer_weights.tid2eid)
  *   ids     : [T x k] int32, device; expert ids per token in selection order
+ *             (table order for a hash-routed layer)
  *   w       : [T x k] fp32, device; renormalised weights, same order, sum 1
  *   offsets : NULL or [E+1] int32, device; exclusive prefix sum of the number
  *             of pairs per expert (offsets[E] = T*k)
  *   perm    : NULL or [T*k] int32, device; pair indices i = t*k + j grouped by
  *             expert id, ascending i inside a group (stable)
- * MOE_ESTATE if the layer's router is not loaded; T = 0 is a no-op. */
-moe_status moe_route(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, int32_t* ids, float* w,
-                     int32_t* offsets, int32_t* perm, void* hip_stream);
+ * MOE_ESTATE if the layer's router is not loaded; MOE_EINVAL if the layer is
+ * hash-routed and token_ids is NULL; T = 0 is a no-op. */
+moe_status moe_route(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const int32_t* token_ids, int32_t* ids,
+                     float* w, int32_t* offsets, int32_t* perm, void* hip_stream);
 
 /* Whole layers (steps 1-5) for T tokens; see moe_fwd_args.  MOE_ESTATE if a
  * layer's router or any of its experts is not loaded, MOE_ERANGE if
@@ -180,7 +202,7 @@ typedef enum {
     MOE_K_DOWN = 3,         /* dequant + down GEMV per expert, decode path */
     MOE_K_COMBINE = 4,      /* ordered weighted combine (+ residual), decode path */
     MOE_K_PF_ROUTER = 5,    /* prefill router */
-    MOE_K_PF_TOPK = 6,      /* prefill top-k + weights */
+    MOE_K_PF_TOPK = 6,      /* prefill top-k + weights (hash-routed layer: table lookup + exact logits of the k ids) */
     MOE_K_PF_SORT = 7,      /* prefill counting sort (three launches: histogram, scan, scatter) */
     MOE_K_PF_GEMM1 = 8,     /* prefill grouped GEMM gate/up + SwiGLU */
     MOE_K_PF_GEMM2 = 9,     /* prefill grouped GEMM down */

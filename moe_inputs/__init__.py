@@ -128,6 +128,19 @@ def gen_experts(seed: int, layer: int, e_begin: int, count: int, H: int, F: int,
     return out
 
 
+def gen_tid2eid(seed: int, layer: int, vocab: int, E: int, k: int) -> np.ndarray:
+    """Hash-routing table [vocab x k] int32: every row k distinct expert ids in
+    [0, E), a seeded uniform choice in a seeded order."""
+    rng = np.random.default_rng([seed, layer, 0x7A1D])
+    return np.argsort(rng.random((vocab, E)), axis=1)[:, :k].astype(np.int32)
+
+
+def gen_token_ids(seed: int, window: int, T: int, vocab: int) -> np.ndarray:
+    """Token ids [T] int32, uniform in [0, vocab)."""
+    rng = np.random.default_rng([seed, window, 0x70C])
+    return rng.integers(0, vocab, T).astype(np.int32)
+
+
 def layer_inputs(cfg: MoEConfig, seed: int, layer: int, raw: bool = False):
     """Router weights, bias and every expert (routed then shared) of one layer."""
     W = gen_router(seed, layer, cfg.E, cfg.H)

@@ -24,7 +24,7 @@ MOE_FWD_PROFILE = 2
 MOE_FWD_PRENORM = 4
 KERNEL_NAMES = {0: "router", 1: "topk_sort", 2: "gateup", 3: "down", 4: "combine", 5: "pf_router", 6: "pf_topk",
                 7: "pf_sort", 8: "pf_gemm1", 9: "pf_gemm2", 10: "pf_combine", 11: "norm"}
-MOE_ABI_VERSION = 1
+MOE_ABI_VERSION = 2
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOMEM", -3: "MOE_EHIP", -4: "MOE_ESTATE", -5: "MOE_ERANGE"}
 
 # Every symbol include/moe.h declares.
@@ -40,13 +40,14 @@ class moe_config(ctypes.Structure):
 class moe_layer_weights(ctypes.Structure):
     _fields_ = [("layer", ctypes.c_int32), ("expert_begin", ctypes.c_int32), ("expert_count", ctypes.c_int32),
                 ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p), ("experts", ctypes.c_void_p),
-                ("experts_bytes", ctypes.c_size_t)]
+                ("experts_bytes", ctypes.c_size_t), ("tid2eid", ctypes.c_void_p), ("vocab", ctypes.c_int32)]
 
 
 class moe_fwd_args(ctypes.Structure):
     _fields_ = [("layer_begin", ctypes.c_int32), ("layer_count", ctypes.c_int32), ("T", ctypes.c_int32),
                 ("flags", ctypes.c_int32), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
-                ("trace_x", ctypes.c_void_p), ("trace_ids", ctypes.c_void_p), ("trace_w", ctypes.c_void_p)]
+                ("trace_x", ctypes.c_void_p), ("trace_ids", ctypes.c_void_p), ("trace_w", ctypes.c_void_p),
+                ("token_ids", ctypes.c_void_p)]
 
 
 class moe_kernel_time(ctypes.Structure):
@@ -72,7 +73,7 @@ def lib():
         vp, i32 = ctypes.c_void_p, ctypes.c_int32
         L.moe_create.argtypes = [ctypes.POINTER(moe_config), ctypes.POINTER(vp)]
         L.moe_load_experts.argtypes = [vp, ctypes.POINTER(moe_layer_weights)]
-        L.moe_route.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, vp]
+        L.moe_route.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, vp, vp]
         L.moe_forward.argtypes = [vp, ctypes.POINTER(moe_fwd_args), vp]
         L.moe_destroy.argtypes = [vp]
         L.moe_last_error.argtypes = []
@@ -129,21 +130,25 @@ def moe_create(hidden, ffn, n_experts, n_shared, top_k, n_layers, quant, max_tok
     return h
 
 
-def moe_load_experts(ctx, layer, router_w=None, router_bias=None, experts=None, expert_begin=0, expert_count=0):
+def moe_load_experts(ctx, layer, router_w=None, router_bias=None, experts=None, expert_begin=0, expert_count=0,
+                     tid2eid=None):
+    if tid2eid is not None and (tid2eid.dtype != np.int32 or tid2eid.ndim != 2):
+        raise ValueError("tid2eid must be a [vocab x k] int32 array")
     w = moe_layer_weights(layer, expert_begin, expert_count, _hptr(router_w), _hptr(router_bias), _hptr(experts),
-                          0 if experts is None else experts.nbytes)
+                          0 if experts is None else experts.nbytes, _hptr(tid2eid),
+                          0 if tid2eid is None else tid2eid.shape[0])
     _check(lib().moe_load_experts(ctx, ctypes.byref(w)))
 
 
-def moe_route(ctx, layer, x, T, ids, w, offsets=None, perm=None, stream=None):
-    _check(lib().moe_route(ctx, layer, _dptr(x), T, _dptr(ids), _dptr(w), _dptr(offsets), _dptr(perm),
-                           _stream(stream)))
+def moe_route(ctx, layer, x, T, ids, w, offsets=None, perm=None, stream=None, token_ids=None):
+    _check(lib().moe_route(ctx, layer, _dptr(x), T, _dptr(token_ids), _dptr(ids), _dptr(w), _dptr(offsets),
+                           _dptr(perm), _stream(stream)))
 
 
 def moe_forward(ctx, x, y, T, layer_begin=0, layer_count=1, flags=0, trace_x=None, trace_ids=None, trace_w=None,
-                stream=None):
+                stream=None, token_ids=None):
     a = moe_fwd_args(layer_begin, layer_count, T, flags, _dptr(x), _dptr(y), _dptr(trace_x), _dptr(trace_ids),
-                     _dptr(trace_w))
+                     _dptr(trace_w), _dptr(token_ids))
     _check(lib().moe_forward(ctx, ctypes.byref(a), _stream(stream)))
 
 
@@ -182,11 +187,12 @@ class MoEContext:
     def expert_bytes(self):
         return moe_expert_bytes(self.H, self.F, self.quant)
 
-    def load(self, layer, router_w=None, router_bias=None, experts=None, expert_begin=0):
+    def load(self, layer, router_w=None, router_bias=None, experts=None, expert_begin=0, tid2eid=None):
+        """tid2eid: None, or a [vocab x k] int32 table that makes the layer hash-routed."""
         count = 0 if experts is None else experts.nbytes // self.expert_bytes
-        moe_load_experts(self.handle, layer, router_w, router_bias, experts, expert_begin, count)
+        moe_load_experts(self.handle, layer, router_w, router_bias, experts, expert_begin, count, tid2eid)
 
-    def route(self, layer, x, stream=None):
+    def route(self, layer, x, stream=None, token_ids=None):
         import torch
         T = x.shape[0]
         dev = x.device
@@ -194,11 +200,11 @@ class MoEContext:
         w = torch.empty((T, self.k), dtype=torch.float32, device=dev)
         offsets = torch.empty(self.E + 1, dtype=torch.int32, device=dev)
         perm = torch.empty(T * self.k, dtype=torch.int32, device=dev)
-        moe_route(self.handle, layer, x, T, ids, w, offsets, perm, stream)
+        moe_route(self.handle, layer, x, T, ids, w, offsets, perm, stream, token_ids)
         return ids, w, offsets, perm
 
     def forward(self, x, layer_begin=0, layer_count=1, residual=False, trace=False, y=None, stream=None,
-                profile=False, prenorm=False):
+                profile=False, prenorm=False, token_ids=None):
         import torch
         T = x.shape[0]
         if y is None:
@@ -210,7 +216,7 @@ class MoEContext:
             tw = torch.empty((layer_count, T, self.k), dtype=torch.float32, device=x.device)
         flags = ((MOE_FWD_RESIDUAL if residual else 0) | (MOE_FWD_PROFILE if profile else 0) |
                  (MOE_FWD_PRENORM if prenorm else 0))
-        moe_forward(self.handle, x, y, T, layer_begin, layer_count, flags, tx, tid, tw, stream)
+        moe_forward(self.handle, x, y, T, layer_begin, layer_count, flags, tx, tid, tw, stream, token_ids)
         return (y, tx, tid, tw) if trace else y
 
     def profile_read(self):

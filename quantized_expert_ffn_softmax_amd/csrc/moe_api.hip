@@ -54,6 +54,8 @@ struct moe_ctx {
     float* biases = nullptr;       // L x E
     std::vector<uint8_t> router_loaded;
     std::vector<uint8_t> expert_loaded;
+    std::vector<int32_t*> tid2eid;  // per layer: NULL (score routing) or the device [vocab x k] hash table
+    std::vector<int32_t> vocab;
     // scratch
     uint8_t* scratch = nullptr;
     size_t scratch_bytes = 0;
@@ -100,6 +102,8 @@ void free_ctx(moe_ctx* c) {
         if (c->stage_done[i]) hipEventDestroy(c->stage_done[i]);
     }
     if (c->load_stream) hipStreamDestroy(c->load_stream);
+    for (int32_t* t : c->tid2eid)
+        if (t) hipFree(t);
     if (c->scratch) hipFree(c->scratch);
     if (c->rstat) hipFree(c->rstat);
     if (c->biases) hipFree(c->biases);
@@ -293,6 +297,8 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     }
     c->router_loaded.assign(L, 0);
     c->expert_loaded.assign((size_t)L * ES, 0);
+    c->tid2eid.assign(L, nullptr);
+    c->vocab.assign(L, 0);
     *out = c;
     return MOE_OK;
 }
@@ -317,7 +323,37 @@ moe_status moe_load_experts(moe_ctx* c, const moe_layer_weights* w) {
         return fail(MOE_EINVAL, "experts_bytes %zu != %d experts x %lld bytes", w->experts_bytes, w->expert_count,
                     (long long)g.canon_expert_bytes);
     if (!w->router_w && w->router_bias) return fail(MOE_EINVAL, "router_bias without router_w");
+    if (w->tid2eid) {
+        if (w->vocab < 1) return fail(MOE_EINVAL, "vocab %d of the hash table is not positive", w->vocab);
+        for (int64_t r = 0; r < w->vocab; ++r) {
+            const int32_t* row = w->tid2eid + r * g.k;
+            for (int j = 0; j < g.k; ++j) {
+                if (row[j] < 0 || row[j] >= g.E)
+                    return fail(MOE_EINVAL, "hash table row %lld: expert %d outside [0, %d)", (long long)r, row[j], g.E);
+                for (int i = 0; i < j; ++i)
+                    if (row[i] == row[j])
+                        return fail(MOE_EINVAL, "hash table row %lld names expert %d twice", (long long)r, row[j]);
+            }
+        }
+    }
     HIP_TRY(c, hipSetDevice(c->cfg.device));
+    if (w->tid2eid) {
+        const size_t tb = (size_t)w->vocab * g.k * 4;
+        if (c->tid2eid[w->layer] && c->vocab[w->layer] != w->vocab) {
+            HIP_TRY(c, hipFree(c->tid2eid[w->layer]));
+            c->tid2eid[w->layer] = nullptr;
+        }
+        if (!c->tid2eid[w->layer]) {
+            if (hipMalloc(&c->tid2eid[w->layer], tb) != hipSuccess) {
+                hipGetLastError();
+                c->tid2eid[w->layer] = nullptr;
+                c->vocab[w->layer] = 0;
+                return fail(MOE_ENOMEM, "hash table of layer %d (%zu bytes) does not fit", w->layer, tb);
+            }
+        }
+        HIP_TRY(c, hipMemcpy(c->tid2eid[w->layer], w->tid2eid, tb, hipMemcpyHostToDevice));
+        c->vocab[w->layer] = w->vocab;
+    }
     if (w->router_w) {
         HIP_TRY(c, hipMemcpy(c->routers + (size_t)w->layer * g.E * g.H, w->router_w, (size_t)g.E * g.H * 2,
                              hipMemcpyHostToDevice));
@@ -391,32 +427,41 @@ moe_status check_layer_ready(moe_ctx* c, int layer, bool need_experts) {
     return MOE_OK;
 }
 
-moe_status route_decode(moe_ctx* c, int layer, const uint16_t* x, int T, int32_t* trace_ids, float* trace_w,
-                        hipStream_t st, bool prof = false) {
+moe_status route_decode(moe_ctx* c, int layer, const uint16_t* x, int T, const int32_t* tok, int32_t* trace_ids,
+                        float* trace_w, hipStream_t st, bool prof = false) {
     const Geom& g = c->g;
     moe_status s = timed(c, prof, MOE_K_ROUTER, layer, st, [&](const Launch& lc) {
         return launch_router_decode(x, T, c->routers + (size_t)layer * g.E * g.H, c->biases + (size_t)layer * g.E, g,
                                     c->rb, lc);
     }, "router kernel launch");
     if (s != MOE_OK) return s;
-    return timed(c, prof, MOE_K_TOPK_SORT, layer, st,
-                 [&](const Launch& lc) { return launch_topk_sort_decode(T, g, c->rb, trace_ids, trace_w, lc); },
-                 "top-k kernel launch");
+    return timed(c, prof, MOE_K_TOPK_SORT, layer, st, [&](const Launch& lc) {
+        return launch_topk_sort_decode(T, g, c->rb, c->tid2eid[layer], tok, c->vocab[layer], trace_ids, trace_w, lc);
+    }, "top-k kernel launch");
 }
 
-moe_status route_prefill(moe_ctx* c, int layer, const uint16_t* x, int T, int32_t* trace_ids, float* trace_w,
-                         hipStream_t st, bool prof = false) {
+moe_status route_prefill(moe_ctx* c, int layer, const uint16_t* x, int T, const int32_t* tok, int32_t* trace_ids,
+                         float* trace_w, hipStream_t st, bool prof = false) {
     const Geom& g = c->g;
     const uint16_t* Wr = c->routers + (size_t)layer * g.E * g.H;
     const float* bias = c->biases + (size_t)layer * g.E;
     const float* rstat = c->rstat + 2 * layer;
-    moe_status s = timed(c, prof, MOE_K_PF_ROUTER, layer, st,
-                         [&](const Launch& lc) { return launch_pf_router(x, T, Wr, bias, g, c->pb, lc); },
-                         "prefill router kernel launch");
-    if (s != MOE_OK) return s;
-    s = timed(c, prof, MOE_K_PF_TOPK, layer, st, [&](const Launch& lc) {
-        return launch_pf_topk(x, T, Wr, bias, rstat, g, c->pb, trace_ids, trace_w, lc);
-    }, "prefill top-k kernel launch");
+    moe_status s;
+    if (c->tid2eid[layer]) {
+        // hash-routed: the ids come from the table, only their k logits are needed
+        s = timed(c, prof, MOE_K_PF_TOPK, layer, st, [&](const Launch& lc) {
+            return launch_pf_hash(x, T, Wr, bias, c->tid2eid[layer], tok, c->vocab[layer], g, c->pb, trace_ids,
+                                  trace_w, lc);
+        }, "prefill hash routing kernel launch");
+    } else {
+        s = timed(c, prof, MOE_K_PF_ROUTER, layer, st,
+                  [&](const Launch& lc) { return launch_pf_router(x, T, Wr, bias, g, c->pb, lc); },
+                  "prefill router kernel launch");
+        if (s != MOE_OK) return s;
+        s = timed(c, prof, MOE_K_PF_TOPK, layer, st, [&](const Launch& lc) {
+            return launch_pf_topk(x, T, Wr, bias, rstat, g, c->pb, trace_ids, trace_w, lc);
+        }, "prefill top-k kernel launch");
+    }
     if (s != MOE_OK) return s;
     s = timed(c, prof, MOE_K_PF_SORT, layer, st, [&](const Launch& lc) { return launch_pf_hist(T, g, c->pb, lc); },
               "prefill histogram kernel launch");
@@ -430,8 +475,8 @@ moe_status route_prefill(moe_ctx* c, int layer, const uint16_t* x, int T, int32_
 
 }  // namespace
 
-moe_status moe_route(moe_ctx* c, int32_t layer, const void* x, int32_t T, int32_t* ids, float* w, int32_t* offsets,
-                     int32_t* perm, void* hip_stream) {
+moe_status moe_route(moe_ctx* c, int32_t layer, const void* x, int32_t T, const int32_t* token_ids, int32_t* ids,
+                     float* w, int32_t* offsets, int32_t* perm, void* hip_stream) {
     if (!c) return fail(MOE_EINVAL, "ctx is NULL");
     if (c->poisoned) return fail(MOE_ESTATE, "context is poisoned by an earlier HIP failure");
     const Geom& g = c->g;
@@ -441,13 +486,15 @@ moe_status moe_route(moe_ctx* c, int32_t layer, const void* x, int32_t T, int32_
     if (T == 0) return MOE_OK;
     if (!x || !ids || !w) return fail(MOE_EINVAL, "x, ids and w are required");
     if (!aligned16(x)) return fail(MOE_EINVAL, "x must be 16-byte aligned");
+    if (c->tid2eid[layer] && (!token_ids || ((uintptr_t)token_ids & 3u)))
+        return fail(MOE_EINVAL, "layer %d is hash-routed: token_ids (4-byte aligned) is required", layer);
     moe_status s = check_layer_ready(c, layer, false);
     if (s != MOE_OK) return s;
     hipStream_t st = (hipStream_t)hip_stream;
     HIP_TRY(c, hipSetDevice(c->cfg.device));
     const bool pf = T > kMaxDecodeT;
-    s = pf ? route_prefill(c, layer, (const uint16_t*)x, T, nullptr, nullptr, st)
-           : route_decode(c, layer, (const uint16_t*)x, T, nullptr, nullptr, st);
+    s = pf ? route_prefill(c, layer, (const uint16_t*)x, T, token_ids, nullptr, nullptr, st)
+           : route_decode(c, layer, (const uint16_t*)x, T, token_ids, nullptr, nullptr, st);
     if (s != MOE_OK) return s;
     const size_t P = (size_t)T * g.k;
     HIP_TRY(c, hipMemcpyAsync(ids, pf ? c->pb.ids : c->rb.ids, P * 4, hipMemcpyDeviceToDevice, st));
@@ -477,6 +524,8 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
     for (int l = a->layer_begin; l < a->layer_begin + a->layer_count; ++l) {
         moe_status s = check_layer_ready(c, l, true);
         if (s != MOE_OK) return s;
+        if (c->tid2eid[l] && (!a->token_ids || ((uintptr_t)a->token_ids & 3u)))
+            return fail(MOE_EINVAL, "layer %d is hash-routed: token_ids (4-byte aligned) is required", l);
     }
     const int T = a->T;
     const bool pf = T > kMaxDecodeT;
@@ -505,7 +554,7 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
         int32_t* tids = a->trace_ids ? a->trace_ids + (size_t)i * T * g.k : nullptr;
         float* tw = a->trace_w ? a->trace_w + (size_t)i * T * g.k : nullptr;
         if (pf) {
-            moe_status s = route_prefill(c, l, xm, T, tids, tw, st, prof);
+            moe_status s = route_prefill(c, l, xm, T, a->token_ids, tids, tw, st, prof);
             if (s != MOE_OK) return s;
             s = timed(c, prof, MOE_K_PF_GEMM1, l, st,
                       [&](const Launch& lc) { return launch_pf_gemm1(xm, T, slots, g, c->pb, lc); },
@@ -521,7 +570,7 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
             xin = yout;
             continue;
         }
-        moe_status s = route_decode(c, l, xm, T, tids, tw, st, prof);
+        moe_status s = route_decode(c, l, xm, T, a->token_ids, tids, tw, st, prof);
         if (s != MOE_OK) return s;
         s = timed(c, prof, MOE_K_GATEUP, l, st,
                   [&](const Launch& lc) { return launch_gateup_decode(xm, T, slots, g, c->rb, c->db, c->maxA, lc); },

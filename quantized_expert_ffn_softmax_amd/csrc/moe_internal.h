@@ -144,8 +144,9 @@ struct Launch {
 hipError_t launch_repack(const uint8_t* canon, uint8_t* slots, int count, const Geom& g, hipStream_t st);
 hipError_t launch_router_decode(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const Geom& g,
                                 RouteBufs rb, const Launch& lc);
-hipError_t launch_topk_sort_decode(int T, const Geom& g, RouteBufs rb, int32_t* trace_ids, float* trace_w,
-                                   const Launch& lc);
+// tab: NULL (score routing) or the layer's [vocab x k] hash table; tok: the tokens' ids
+hipError_t launch_topk_sort_decode(int T, const Geom& g, RouteBufs rb, const int32_t* tab, const int32_t* tok, int vocab,
+                                   int32_t* trace_ids, float* trace_w, const Launch& lc);
 hipError_t launch_gateup_decode(const uint16_t* x, int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb,
                                 DecodeBufs db, int maxA, const Launch& lc);
 hipError_t launch_down_decode(int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb, DecodeBufs db, int maxA,
@@ -163,6 +164,10 @@ hipError_t launch_pf_router(const uint16_t* x, int T, const uint16_t* Wr, const 
                             PrefillBufs pb, const Launch& lc);
 hipError_t launch_pf_topk(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const float* rstat,
                           const Geom& g, PrefillBufs pb, int32_t* trace_ids, float* trace_w, const Launch& lc);
+// Hash-routed prefill layer: ids from the table, exact logits of those ids, weights.
+hipError_t launch_pf_hash(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const int32_t* tab,
+                          const int32_t* tok, int vocab, const Geom& g, PrefillBufs pb, int32_t* trace_ids,
+                          float* trace_w, const Launch& lc);
 hipError_t launch_pf_hist(int T, const Geom& g, PrefillBufs pb, const Launch& lc);
 hipError_t launch_pf_scan(int T, const Geom& g, PrefillBufs pb, const Launch& lc);
 hipError_t launch_pf_scatter(int T, const Geom& g, PrefillBufs pb, const Launch& lc);

@@ -237,7 +237,9 @@ hipError_t launch_router_decode(const uint16_t* x, int T, const uint16_t* Wr, co
 // the number of tokens t' < t that chose e, and the group size is popc(mask).
 template <int J>
 __global__ __launch_bounds__(256) void k_topk_sort(int T, int E, int k, int S, RouteBufs rb,
-                                                   int32_t* __restrict__ trace_ids, float* __restrict__ trace_w) {
+                                                   const int32_t* __restrict__ tab, const int32_t* __restrict__ tok,
+                                                   int vocab, int32_t* __restrict__ trace_ids,
+                                                   float* __restrict__ trace_w) {
     __shared__ uint32_t s_mask[kMaxExperts];
     __shared__ int32_t s_off[kMaxExperts];
     __shared__ int32_t s_aidx[kMaxExperts];
@@ -268,7 +270,15 @@ __global__ __launch_bounds__(256) void k_topk_sort(int T, int E, int k, int S, R
         if (t >= T) break;
         int my_e = 0;
         double my_l = 0.0;
-        if (wave_topk_fast<J>(raw[r2], E, k, lane, my_e)) {
+        double l0;
+        if (tab) {
+            // hash-routed layer: the experts are row tok[t] of the table, in table order
+            my_e = lane < k ? tab[(int64_t)min(max(tok[t], 0), vocab - 1) * k + lane] : 0;
+            my_l = lane < k ? rb.logits[(int64_t)t * E + my_e] : -HUGE_VAL;
+            l0 = my_l;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) l0 = fmax(l0, __shfl_xor(l0, o));
+        } else if (wave_topk_fast<J>(raw[r2], E, k, lane, my_e)) {
             // the exact fp64 logits of the selected experts, from this wave's copy in LDS
 #pragma unroll
             for (int j = 0; j < J; ++j) s_lg[wave][lane + 64 * j] = raw[r2][j];
@@ -296,7 +306,7 @@ __global__ __launch_bounds__(256) void k_topk_sort(int T, int E, int k, int S, R
                 if (lane == r) { my_l = key_value(bk); my_e = be; }
             }
         }
-        const double l0 = __shfl(my_l, 0);
+        if (!tab) l0 = __shfl(my_l, 0);  // rank 0 holds the largest selected logit
         // renormalised softmax over the selected logits (fp64)
         const double ex = lane < k ? exp(my_l - l0) : 0.0;
         const double z = wave_sum_f64(ex);
@@ -364,14 +374,14 @@ __global__ __launch_bounds__(256) void k_topk_sort(int T, int E, int k, int S, R
     for (int i = tid; i < (U + S) * kMaxDecodeT; i += blockDim.x) rb.wtab[i] = s_wtab[i];
 }
 
-hipError_t launch_topk_sort_decode(int T, const Geom& g, RouteBufs rb, int32_t* trace_ids, float* trace_w,
-                                   const Launch& lc) {
+hipError_t launch_topk_sort_decode(int T, const Geom& g, RouteBufs rb, const int32_t* tab, const int32_t* tok, int vocab,
+                                   int32_t* trace_ids, float* trace_w, const Launch& lc) {
     if (g.E <= 256)
-        launch(k_topk_sort<4>, dim3(1), dim3(256), 0, lc, T, g.E, g.k, g.S, rb, trace_ids, trace_w);
+        launch(k_topk_sort<4>, dim3(1), dim3(256), 0, lc, T, g.E, g.k, g.S, rb, tab, tok, vocab, trace_ids, trace_w);
     else if (g.E <= 512)
-        launch(k_topk_sort<8>, dim3(1), dim3(256), 0, lc, T, g.E, g.k, g.S, rb, trace_ids, trace_w);
+        launch(k_topk_sort<8>, dim3(1), dim3(256), 0, lc, T, g.E, g.k, g.S, rb, tab, tok, vocab, trace_ids, trace_w);
     else
-        launch(k_topk_sort<16>, dim3(1), dim3(256), 0, lc, T, g.E, g.k, g.S, rb, trace_ids, trace_w);
+        launch(k_topk_sort<16>, dim3(1), dim3(256), 0, lc, T, g.E, g.k, g.S, rb, tab, tok, vocab, trace_ids, trace_w);
     return hipGetLastError();
 }
 

@@ -136,6 +136,37 @@ __global__ __launch_bounds__(256) void k_pf_router(const uint16_t* __restrict__ 
 // exact one, and any expert whose fp32 logit is below L_k - 2 tol (L_k the
 // k-th largest fp32 logit) is beaten exactly by each of the k fp32 leaders:
 // the exact top-k lies inside the candidate set.
+// Exact logits of experts ea and eb for the token whose x row the wave holds
+// in xv (lane l: elements 8 l + 512 i .. +7, zero past H): the fp64 sum of the
+// exact bf16 x bf16 products in a fixed order (per lane, then the wave tree),
+// plus the bias.  The result is wave-uniform.
+__device__ __forceinline__ void exact_logit2(const u32x4_t (&xv)[8], const uint16_t* __restrict__ Wr,
+                                             const float* __restrict__ bias, int H, int lane, int ea, int eb,
+                                             double& sa, double& sb) {
+    const uint16_t* wa = Wr + (int64_t)ea * H;
+    const uint16_t* wb = Wr + (int64_t)eb * H;
+    sa = 0.0;
+    sb = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (512 * i < H) {
+            const int h0 = min(lane * 8 + 512 * i, H - 8);  // lanes past H hold x = 0
+            const u32x4_t va = *reinterpret_cast<const u32x4_t*>(wa + h0);
+            const u32x4_t vb = *reinterpret_cast<const u32x4_t*>(wb + h0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float x0 = bf2f(xv[i][q] & 0xFFFFu), x1 = bf2f(xv[i][q] >> 16);
+                sa += (double)(x0 * bf2f(va[q] & 0xFFFFu));
+                sa += (double)(x1 * bf2f(va[q] >> 16));
+                sb += (double)(x0 * bf2f(vb[q] & 0xFFFFu));
+                sb += (double)(x1 * bf2f(vb[q] >> 16));
+            }
+        }
+    }
+    sa = wave_sum_f64(sa) + (bias ? (double)bias[ea] : 0.0);
+    sb = wave_sum_f64(sb) + (bias ? (double)bias[eb] : 0.0);
+}
+
 template <int J>
 __global__ __launch_bounds__(256) void k_pf_topk(const uint16_t* __restrict__ x, int T,
                                                  const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
@@ -206,27 +237,8 @@ __global__ __launch_bounds__(256) void k_pf_topk(const uint16_t* __restrict__ x,
     // exact logits of the candidates, two per pass
     for (int r = 0; r < nc; r += 2) {
         const int ea = s_e[wave][r], eb = s_e[wave][min(r + 1, nc - 1)];
-        const uint16_t* wa = Wr + (int64_t)ea * H;
-        const uint16_t* wb = Wr + (int64_t)eb * H;
-        double sa = 0.0, sb = 0.0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if (512 * i < H) {
-                const int h0 = min(lane * 8 + 512 * i, H - 8);  // lanes past H hold x = 0
-                const u32x4_t va = *reinterpret_cast<const u32x4_t*>(wa + h0);
-                const u32x4_t vb = *reinterpret_cast<const u32x4_t*>(wb + h0);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float x0 = bf2f(xv[i][q] & 0xFFFFu), x1 = bf2f(xv[i][q] >> 16);
-                    sa += (double)(x0 * bf2f(va[q] & 0xFFFFu));
-                    sa += (double)(x1 * bf2f(va[q] >> 16));
-                    sb += (double)(x0 * bf2f(vb[q] & 0xFFFFu));
-                    sb += (double)(x1 * bf2f(vb[q] >> 16));
-                }
-            }
-        }
-        sa = wave_sum_f64(sa) + (bias ? (double)bias[ea] : 0.0);
-        sb = wave_sum_f64(sb) + (bias ? (double)bias[eb] : 0.0);
+        double sa, sb;
+        exact_logit2(xv, Wr, bias, H, lane, ea, eb, sa, sb);
         if (lane == 0) {
             s_l[wave][r] = sa;
             if (r + 1 < nc) s_l[wave][r + 1] = sb;
@@ -262,6 +274,55 @@ __global__ __launch_bounds__(256) void k_pf_topk(const uint16_t* __restrict__ x,
     }
     // weights: softmax over the k selected exact logits (lane r holds rank r)
     const double lmax = __shfl(my_l, 0);
+    const double ex = lane < k ? exp(my_l - lmax) : 0.0;
+    const double z = wave_sum_f64(ex);
+    if (lane < k) {
+        const float wv = (float)(ex / z);
+        pb.ids[(int64_t)t * k + lane] = my_e;
+        pb.w[(int64_t)t * k + lane] = wv;
+        if (trace_ids) trace_ids[(int64_t)t * k + lane] = my_e;
+        if (trace_w) trace_w[(int64_t)t * k + lane] = wv;
+    }
+}
+
+// Hash-routed layer, one wave per token: the experts of token t are row
+// tok[t] (clamped into [0, vocab)) of the [vocab x k] table, in table order;
+// their exact logits give the weights (softmax over the k logits, which is
+// the softmax over all E renormalised over them).  No other logit is needed,
+// so the layer's router GEMM does not run.
+__global__ __launch_bounds__(256) void k_pf_hash(const uint16_t* __restrict__ x, int T,
+                                                 const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
+                                                 const int32_t* __restrict__ tab, const int32_t* __restrict__ tok,
+                                                 int vocab, int H, int k, PrefillBufs pb,
+                                                 int32_t* __restrict__ trace_ids, float* __restrict__ trace_w) {
+    __shared__ double s_l[4][kMaxTopK];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;  // no workgroup barrier below
+    const uint16_t* xr = x + (int64_t)t * H;
+    u32x4_t xv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int h0 = lane * 8 + 512 * i;
+        xv[i] = u32x4_t{0u, 0u, 0u, 0u};
+        if (h0 < H) xv[i] = *reinterpret_cast<const u32x4_t*>(xr + h0);
+    }
+    const int32_t* ids = tab + (int64_t)min(max(tok[t], 0), vocab - 1) * k;
+    for (int r = 0; r < k; r += 2) {
+        double sa, sb;
+        exact_logit2(xv, Wr, bias, H, lane, ids[r], ids[min(r + 1, k - 1)], sa, sb);
+        if (lane == 0) {
+            s_l[wave][r] = sa;
+            if (r + 1 < k) s_l[wave][r + 1] = sb;
+        }
+    }
+    wave_lds_sync();
+    const double my_l = lane < k ? s_l[wave][lane] : -HUGE_VAL;
+    const int my_e = lane < k ? ids[lane] : 0;
+    double lmax = my_l;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) lmax = fmax(lmax, __shfl_xor(lmax, o));
     const double ex = lane < k ? exp(my_l - lmax) : 0.0;
     const double z = wave_sum_f64(ex);
     if (lane < k) {
@@ -799,6 +860,14 @@ hipError_t launch_pf_topk(const uint16_t* x, int T, const uint16_t* Wr, const fl
         launch(k_pf_topk<8>, grid, dim3(256), 0, lc, x, T, Wr, bias, rstat, g.E, g.H, g.k, pb, trace_ids, trace_w);
     else
         launch(k_pf_topk<16>, grid, dim3(256), 0, lc, x, T, Wr, bias, rstat, g.E, g.H, g.k, pb, trace_ids, trace_w);
+    return hipGetLastError();
+}
+
+hipError_t launch_pf_hash(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const int32_t* tab,
+                          const int32_t* tok, int vocab, const Geom& g, PrefillBufs pb, int32_t* trace_ids,
+                          float* trace_w, const Launch& lc) {
+    launch(k_pf_hash, dim3((T + 3) / 4), dim3(256), 0, lc, x, T, Wr, bias, tab, tok, vocab, g.H, g.k, pb, trace_ids,
+           trace_w);
     return hipGetLastError();
 }
 

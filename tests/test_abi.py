@@ -41,7 +41,7 @@ def test_host_only_calls_without_gpu():
     lib = moe.lib()
     assert lib.moe_destroy(None) == moe.MOE_OK
     assert lib.moe_forward(None, None, None) == moe.MOE_EINVAL
-    assert lib.moe_route(None, 0, None, 1, None, None, None, None, None) == moe.MOE_EINVAL
+    assert lib.moe_route(None, 0, None, 1, None, None, None, None, None, None) == moe.MOE_EINVAL
     assert lib.moe_load_experts(None, None) == moe.MOE_EINVAL
     assert b"NULL" in lib.moe_last_error()
     # a bad geometry is rejected before any device is touched
@@ -51,3 +51,30 @@ def test_host_only_calls_without_gpu():
     assert h.value is None
     cfg = moe.moe_config(99, 128, 64, 8, 0, 2, 1, moe.MOE_Q4B32, 4, 0)
     assert lib.moe_create(ctypes.byref(cfg), ctypes.byref(h)) == moe.MOE_EINVAL
+
+
+def test_binding_struct_layouts_match_the_header(tmp_path):
+    """The ctypes structures of the binding have the sizes and field offsets a C
+    compiler gives the structures of include/moe.h."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    src = tmp_path / "layout.c"
+    fields = {"moe_config": ["abi_version", "max_tokens", "device"],
+              "moe_layer_weights": ["layer", "router_w", "router_bias", "experts", "experts_bytes", "tid2eid", "vocab"],
+              "moe_fwd_args": ["layer_begin", "flags", "x", "y", "trace_x", "trace_ids", "trace_w", "token_ids"],
+              "moe_kernel_time": ["kernel", "layer", "ms"]}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "moe.h"', "int main(void) {"]
+    for st, fs in fields.items():
+        lines.append(f'    printf("{st} %zu\\n", sizeof({st}));')
+        for f in fs:
+            lines.append(f'    printf("{st}.{f} %zu\\n", offsetof({st}, {f}));')
+    lines += ["    return 0;", "}"]
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(root, "include"), "-o", str(exe), str(src)], check=True)
+    got = dict(ln.split() for ln in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines())
+    for st, fs in fields.items():
+        cls = getattr(moe, st)
+        assert int(got[st]) == ctypes.sizeof(cls), st
+        for f in fs:
+            assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, f"{st}.{f}"
