@@ -427,12 +427,13 @@ moe_status check_layer_ready(moe_ctx* c, int layer, bool need_experts) {
     return MOE_OK;
 }
 
+// hm != NULL: x is the raw stream, the router writes its pre-norm to hm and routes on it
 moe_status route_decode(moe_ctx* c, int layer, const uint16_t* x, int T, const int32_t* tok, int32_t* trace_ids,
-                        float* trace_w, hipStream_t st, bool prof = false) {
+                        float* trace_w, hipStream_t st, bool prof = false, uint16_t* hm = nullptr) {
     const Geom& g = c->g;
     moe_status s = timed(c, prof, MOE_K_ROUTER, layer, st, [&](const Launch& lc) {
         return launch_router_decode(x, T, c->routers + (size_t)layer * g.E * g.H, c->biases + (size_t)layer * g.E, g,
-                                    c->rb, lc);
+                                    c->rb, hm, lc);
     }, "router kernel launch");
     if (s != MOE_OK) return s;
     return timed(c, prof, MOE_K_TOPK_SORT, layer, st, [&](const Launch& lc) {
@@ -539,16 +540,20 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
         const bool last = i == a->layer_count - 1;
         uint16_t* yout = last ? (uint16_t*)a->y : c->xbuf[i & 1];
         const bool prof = (a->flags & MOE_FWD_PROFILE) != 0;
-        // xm: the MoE input of this layer (the normalised stream with MOE_FWD_PRENORM); the residual adds to xin
+        // xm: the MoE input of this layer (the normalised stream with MOE_FWD_PRENORM); the residual adds to xin.
+        // Decode windows normalise inside the router kernel (no separate launch).
         const uint16_t* xm = xin;
-        if (a->flags & MOE_FWD_PRENORM) {
+        const bool fused_norm = !pf && (a->flags & MOE_FWD_PRENORM);
+        if (fused_norm) {
+            xm = c->hbuf;
+        } else if (a->flags & MOE_FWD_PRENORM) {
             moe_status s = timed(c, prof, MOE_K_NORM, l, st,
                                  [&](const Launch& lc) { return launch_rmsnorm(xin, T, g.H, c->hbuf, lc); },
                                  "pre-norm kernel launch");
             if (s != MOE_OK) return s;
             xm = c->hbuf;
         }
-        if (a->trace_x)
+        if (a->trace_x && !fused_norm)
             HIP_TRY(c, hipMemcpyAsync((uint8_t*)a->trace_x + (size_t)i * xbytes, xm, xbytes, hipMemcpyDeviceToDevice, st));
         const uint8_t* slots = c->arena + (size_t)l * ES * g.slot_bytes;
         int32_t* tids = a->trace_ids ? a->trace_ids + (size_t)i * T * g.k : nullptr;
@@ -570,8 +575,11 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
             xin = yout;
             continue;
         }
-        moe_status s = route_decode(c, l, xm, T, a->token_ids, tids, tw, st, prof);
+        moe_status s = fused_norm ? route_decode(c, l, xin, T, a->token_ids, tids, tw, st, prof, c->hbuf)
+                                  : route_decode(c, l, xm, T, a->token_ids, tids, tw, st, prof);
         if (s != MOE_OK) return s;
+        if (a->trace_x && fused_norm)
+            HIP_TRY(c, hipMemcpyAsync((uint8_t*)a->trace_x + (size_t)i * xbytes, xm, xbytes, hipMemcpyDeviceToDevice, st));
         s = timed(c, prof, MOE_K_GATEUP, l, st,
                   [&](const Launch& lc) { return launch_gateup_decode(xm, T, slots, g, c->rb, c->db, c->maxA, lc); },
                   "gate/up kernel launch");

@@ -142,8 +142,10 @@ struct Launch {
 
 // Launchers (return hipGetLastError()).
 hipError_t launch_repack(const uint8_t* canon, uint8_t* slots, int count, const Geom& g, hipStream_t st);
+// hm: NULL, or [T x H] bf16 that receives the per-token RMS pre-norm of x, which
+// the router then routes on (fused pre-norm of a decode chain layer)
 hipError_t launch_router_decode(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const Geom& g,
-                                RouteBufs rb, const Launch& lc);
+                                RouteBufs rb, uint16_t* hm, const Launch& lc);
 // tab: NULL (score routing) or the layer's [vocab x k] hash table; tok: the tokens' ids
 hipError_t launch_topk_sort_decode(int T, const Geom& g, RouteBufs rb, const int32_t* tab, const int32_t* tok, int vocab,
                                    int32_t* trace_ids, float* trace_w, const Launch& lc);

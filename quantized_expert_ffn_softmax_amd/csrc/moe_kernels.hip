@@ -136,14 +136,23 @@ hipError_t launch_repack(const uint8_t* canon, uint8_t* slots, int count, const 
 // segments of its quarter (NJ = ceil(H / 2048)) and requests the router
 // row's segments and the TT token rows' segments (TT = T rounded up to a power
 // of two; rows past T repeat the last) all at once, before any math.
+// PRE: the layer's input is the per-token unit-gain RMS pre-norm of x,
+// h = bf16(x / sqrt(mean(x^2) + eps)) (fp32; sum of squares per lane, wave
+// tree, the four quarters in a fixed order): every workgroup computes the same
+// scales from the rows it holds, normalises them in registers, and workgroup 0
+// writes h to hm for the expert kernels (so the separate pre-norm launch of a
+// chain layer is not needed).
 // All threads of the grid also share the per-block sums
-// sx[b][m] = sum_{q<32} x[m][32b+q] (fp32, in q order; zero for m >= T).
-template <int NJ, int TT>
+// sx[b][m] = sum_{q<32} in[m][32b+q] of the layer input (x, or h with PRE;
+// fp32, in q order; zero for m >= T).
+template <int NJ, int TT, bool PRE>
 __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restrict__ x, int T,
                                                        const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
                                                        int E, int H, int nbp, double* __restrict__ logits,
-                                                       float* __restrict__ sx) {
+                                                       float* __restrict__ sx, uint16_t* __restrict__ hm) {
     __shared__ double s_part[4][TT];
+    __shared__ float s_ss[4][TT];
+    __shared__ float s_r[kMaxDecodeT];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int e = blockIdx.x;
@@ -157,6 +166,48 @@ __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restric
 #pragma unroll
         for (int t = 0; t < TT; ++t)
             xv[j][t] = *reinterpret_cast<const u32x4_t*>(x + (int64_t)min(t, T - 1) * H + h0 + 8 * seg);
+    }
+    if constexpr (PRE) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            float ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                if (lane + 64 * j < ns) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float lo = __uint_as_float(xv[j][t][q] << 16);
+                        const float hi = __uint_as_float(xv[j][t][q] & 0xFFFF0000u);
+                        ss = fmaf(lo, lo, ss);
+                        ss = fmaf(hi, hi, ss);
+                    }
+                }
+            }
+            ss = row_sum_f32(ss);
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+            if (lane == 0) s_ss[wave][t] = ss;
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < TT) {
+            const int t = threadIdx.x;
+            const float tot = (s_ss[0][t] + s_ss[1][t]) + (s_ss[2][t] + s_ss[3][t]);
+            s_r[t] = 1.0f / sqrtf(tot / (float)H + kNormEps);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            const float r = s_r[t];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    xv[j][t][q] = pack_bf16(__uint_as_float(xv[j][t][q] << 16) * r,
+                                            __uint_as_float(xv[j][t][q] & 0xFFFF0000u) * r);
+                if (blockIdx.x == 0 && t < T && lane + 64 * j < ns)
+                    *reinterpret_cast<u32x4_t*>(hm + (int64_t)t * H + h0 + 8 * (lane + 64 * j)) = xv[j][t];
+            }
+        }
     }
     double acc[TT];
 #pragma unroll
@@ -197,13 +248,21 @@ __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restric
         float s = 0.f;
         if (m < T && b < nb) {
             const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (int64_t)m * H + b * 32);
+            const float r = PRE ? s_r[m] : 1.0f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const u32x4_t v = xr[r];
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const u32x4_t v = xr[q4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    s += __uint_as_float(v[q] << 16);
-                    s += __uint_as_float(v[q] & 0xFFFF0000u);
+                    if constexpr (PRE) {
+                        const uint32_t hv = pack_bf16(__uint_as_float(v[q] << 16) * r,
+                                                      __uint_as_float(v[q] & 0xFFFF0000u) * r);
+                        s += __uint_as_float(hv << 16);
+                        s += __uint_as_float(hv & 0xFFFF0000u);
+                    } else {
+                        s += __uint_as_float(v[q] << 16);
+                        s += __uint_as_float(v[q] & 0xFFFF0000u);
+                    }
                 }
             }
         }
@@ -212,14 +271,18 @@ __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restric
 }
 
 hipError_t launch_router_decode(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const Geom& g,
-                                RouteBufs rb, const Launch& lc) {
+                                RouteBufs rb, uint16_t* hm, const Launch& lc) {
     const dim3 grid(g.E);
     const int nj = (g.H / 32 + 63) / 64;  // 1 or 2 (H <= 4096)
-#define MOE_ROUTER_CASE(NJ, TT)                                                                                    \
-    if (nj == NJ && T <= TT) {                                                                                     \
-        launch(k_router_decode<NJ, TT>, grid, dim3(256), 0, lc, x, T, Wr, bias, g.E, g.H, g.gu.nch * 4, rb.logits, \
-               rb.sx);                                                                                             \
-        return hipGetLastError();                                                                                  \
+#define MOE_ROUTER_CASE(NJ, TT)                                                                                     \
+    if (nj == NJ && T <= TT) {                                                                                      \
+        if (hm)                                                                                                     \
+            launch(k_router_decode<NJ, TT, true>, grid, dim3(256), 0, lc, x, T, Wr, bias, g.E, g.H, g.gu.nch * 4,   \
+                   rb.logits, rb.sx, hm);                                                                           \
+        else                                                                                                        \
+            launch(k_router_decode<NJ, TT, false>, grid, dim3(256), 0, lc, x, T, Wr, bias, g.E, g.H, g.gu.nch * 4,  \
+                   rb.logits, rb.sx, hm);                                                                           \
+        return hipGetLastError();                                                                                   \
     }
     MOE_ROUTER_CASE(1, 1) MOE_ROUTER_CASE(1, 2) MOE_ROUTER_CASE(1, 4) MOE_ROUTER_CASE(1, 8)
     MOE_ROUTER_CASE(2, 1) MOE_ROUTER_CASE(2, 2) MOE_ROUTER_CASE(2, 4) MOE_ROUTER_CASE(2, 8)
@@ -745,7 +808,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const uint16_t* __restrict__ x,
         u32x4_t o;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            o[q] = f2bf(bf2f(v[q] & 0xFFFFu) * r) | (f2bf(bf2f(v[q] >> 16) * r) << 16);
+            o[q] = pack_bf16(bf2f(v[q] & 0xFFFFu) * r, bf2f(v[q] >> 16) * r);
         hr[i] = o;
     }
 }
