@@ -38,7 +38,10 @@ namespace moe {
 // One chunk (4 blocks) of a 16-row tile against A operands A[0..3]:
 //   acc[i] += sum_j d[n][j] * sum_k A[m][k] (128 + q[n][k])
 //   corr   += S[m][4c+g] * d[n][4c+g]     (v_mfma_f32_16x16x4f32, K = the 4 blocks)
-template <int FMT>
+// Only the first NV result registers are scaled and accumulated (a lane's
+// register i holds output row 4 (lane / 16) + i; callers that leave rows
+// 4 g + i, i >= NV, zero need only NV of them).
+template <int FMT, int NV = 4>
 __device__ __forceinline__ void chunk_mac(const uint32_t* cw, u32x2_t sc, const u32x4_t* A, float s_corr, int g,
                                          f32x4_t& acc, f32x4_t& corr) {
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
@@ -46,10 +49,8 @@ __device__ __forceinline__ void chunk_mac(const uint32_t* cw, u32x2_t sc, const 
     for (int j = 0; j < 4; ++j) {
         f32x4_t R = mfma_bf16(A[j], unpack<FMT>(cw, j, bf16_bias_bits()), zero);
         const float d = scale_of(sc, j);
-        acc[0] += d * R[0];
-        acc[1] += d * R[1];
-        acc[2] += d * R[2];
-        acc[3] += d * R[3];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc[i] += d * R[i];
     }
     corr = mfma_f32(s_corr, scale_of(sc, g), corr);
 }
@@ -458,13 +459,16 @@ hipError_t launch_topk_sort_decode(int T, const Geom& g, RouteBufs rb, const int
 // issue all their loads on entry (unconditional, indices clamped, so the
 // compiler counts them) right after the workgroup's share of x, which is
 // written to LDS as soon as it arrives, with the weights still in flight.
-// The MFMA computes C[m = token][n = row] with A = x (rows m >= T zero).
+// The MFMA computes C[m][n = row] with A = x: row m = 4 g + i carries token
+// R g + i for i < R (R = 1 for T <= 4, else 2) and reads the zero row
+// otherwise, so a lane's results for its tokens sit in its first R result
+// registers and only those are scaled.
 // Output: v = w_t,a * silu(g) * u as the bf16 hi/lo A fragments of the down
 // projection, and their per-half-block sums.
 // (slots and sx are deliberately not __restrict__: with it the compiler may
 // treat their loads as invariant and sink them past the barrier into the
 // branch that uses them, which serialises the weight stream behind staging.)
-template <int FMT, int NC, int XPER>
+template <int FMT, int NC, int XPER, int R>
 __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restrict__ x, int T,
                                                        const uint8_t* slots, Geom g,
                                                        const float* sx, const int32_t* __restrict__ nact,
@@ -480,6 +484,7 @@ __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restric
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, gs = lane >> 4, m = lane & 15;
+    const int mt = (m & 3) < R ? R * (m >> 2) + (m & 3) : 15;  // token of A row m (T <= 8: 15 is no token)
     const MatGeom& mg = g.gu;
     const int c0 = wave * mg.nch / 4, c1 = (wave + 1) * mg.nch / 4;
     constexpr int CWN = FMT == 1 ? 4 : 2;
@@ -493,7 +498,7 @@ __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restric
     u32x2_t sg[NC], su[NC];
     float sxv[NC];
 #pragma unroll
-    for (int j = 0; j < NC; ++j) sxv[j] = sx[(min(c0 + j, mg.nch - 1) * 4 + gs) * 16 + m];
+    for (int j = 0; j < NC; ++j) sxv[j] = sx[(min(c0 + j, mg.nch - 1) * 4 + gs) * 16 + mt];
     __builtin_amdgcn_sched_barrier(0);
     // chunk by chunk (scheduling barriers keep the order), so the math on
     // chunk j can start as soon as chunk j has arrived
@@ -507,9 +512,10 @@ __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restric
         su[j] = load_scales(Ut + off, QF<FMT>::kCW, n);
         __builtin_amdgcn_sched_barrier(0);
     }
-    // routing weights of this expert's tokens (used by wave 0 in the epilogue)
-    const f32x4_t wt0 = *reinterpret_cast<const f32x4_t*>(wtab + a * kMaxDecodeT);
-    const f32x4_t wt1 = *reinterpret_cast<const f32x4_t*>(wtab + a * kMaxDecodeT + 4);
+    // routing weights of this lane's tokens R gs + i (used by wave 0 in the epilogue)
+    float wt[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) wt[i] = wtab[a * kMaxDecodeT + R * gs + i];
     const int xstride = g.H + 8;
     // [T + 1][H + 8]: rows padded against bank conflicts; row T is zero and is
     // what the MFMA rows m >= T read, so the A operands need no masking
@@ -527,7 +533,7 @@ __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restric
         }, (T + 1) * xs8);
     }
     __syncthreads();
-    const uint16_t* xl = xs + (m < T ? m : T) * xstride + 8 * gs;
+    const uint16_t* xl = xs + (mt < T ? mt : T) * xstride + 8 * gs;
     f32x4_t accG = {0.f, 0.f, 0.f, 0.f}, accU = accG, corG = accG, corU = accG;
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
@@ -539,8 +545,8 @@ __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restric
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 A[q] = *reinterpret_cast<const u32x4_t*>(xl + min(c * 4 + q, mg.nb - 1) * 32);
-            chunk_mac<FMT>(cg[j], sg[j], A, sxv[j], gs, accG, corG);
-            chunk_mac<FMT>(cu[j], su[j], A, sxv[j], gs, accU, corU);
+            chunk_mac<FMT, R>(cg[j], sg[j], A, sxv[j], gs, accG, corG);
+            chunk_mac<FMT, R>(cu[j], su[j], A, sxv[j], gs, accU, corU);
         }
     }
     // waves 1..3 hand their partial sums to wave 0 through the LDS area x occupied
@@ -561,58 +567,70 @@ __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restric
         corG += red[(w * 4 + 2) * 64 + lane];
         corU += red[(w * 4 + 3) * 64 + lane];
     }
-    // lane holds (token t = 4*gs + i, row f = 16*rt + n); tokens < 8 live in gs 0..1.
-    // v = w * silu(g) * u becomes the down projection's A operand: rows m = t
-    // (bf16 hi) and 8 + t (bf16 lo), k = f, in the layout of one MFMA fragment
-    // per 32-wide block of F, plus the per-half-block row sums of both halves.
+    // lane holds (token t = R gs + i, row f = 16 rt + n) in result register i < R.
+    // v = w * silu(g) * u becomes the down projection's A operand, k = f, in
+    // the layout of one MFMA fragment per 32-wide block of F: token t's bf16 hi
+    // part in row 4 (t % 4) + 2 (t / 4) and its bf16 lo part in the row after,
+    // plus the per-half-block row sums of both parts.  All 16 rows are written
+    // (zeros for t >= T): with R = 1 lane group gs also writes the zero rows of
+    // token gs + 4.
     const int nbFp = g.dn.nch * 4;
     const int bF = rt >> 1, kf = 16 * (rt & 1) + n;
-    uint16_t* af16 = reinterpret_cast<uint16_t*>(afrag) + ((int64_t)a * nbFp + bF) * 64 * 8;
-    float shi[4], slo[4];
+    uint16_t* af16 = reinterpret_cast<uint16_t*>(afrag) + ((int64_t)a * nbFp + bF) * 64 * 8 + 16 * (kf >> 3) * 8 +
+                     (kf & 7);
+    float shi[R], slo[R];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = 4 * gs + i;
+    for (int i = 0; i < R; ++i) {
+        const int t = R * gs + i;
         const float gv = accG[i] - QF<FMT>::kBias * corG[i];
         const float uv = accU[i] - QF<FMT>::kBias * corU[i];
         const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-        const float wv = gs == 0 ? wt0[i] : wt1[i];
-        const float v = t < T ? wv * h : 0.f;  // rows t >= T are written as zeros
+        const float v = t < T ? wt[i] * h : 0.f;  // rows t >= T are written as zeros
         const uint32_t hi = f2bf(v);
         const uint32_t lo = f2bf(v - bf2f(hi));
-        shi[i] = bf2f(hi);
-        slo[i] = bf2f(lo);
-        if (gs < 2) {
-            af16[(t + 16 * (kf >> 3)) * 8 + (kf & 7)] = (uint16_t)hi;
-            af16[(8 + t + 16 * (kf >> 3)) * 8 + (kf & 7)] = (uint16_t)lo;
-        }
+        shi[i] = row_sum_f32(bf2f(hi));
+        slo[i] = row_sum_f32(bf2f(lo));
+        const int rh = 4 * (t & 3) + 2 * (t >> 2);
+        af16[rh * 8] = (uint16_t)hi;
+        af16[(rh + 1) * 8] = (uint16_t)lo;
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        shi[i] = row_sum_f32(shi[i]);
-        slo[i] = row_sum_f32(slo[i]);
+    if constexpr (R == 1) {  // token gs + 4: rows 4 gs + 2, 4 gs + 3
+        af16[(4 * gs + 2) * 8] = 0;
+        af16[(4 * gs + 3) * 8] = 0;
     }
-    if (n == 0 && gs < 2) {
+    if (n == 0) {
         float* sp = spart + (((int64_t)a * nbFp + bF) * 2 + (rt & 1)) * 16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 4 * gs + i;
-            sp[t] = shi[i];
-            sp[8 + t] = slo[i];
+        for (int i = 0; i < R; ++i) {
+            const int t = R * gs + i, rh = 4 * (t & 3) + 2 * (t >> 2);
+            sp[rh] = shi[i];
+            sp[rh + 1] = slo[i];
+        }
+        if constexpr (R == 1) {
+            sp[4 * gs + 2] = 0.f;
+            sp[4 * gs + 3] = 0.f;
         }
     }
+}
+
+template <int FMT, int NC, int XPER, int R>
+hipError_t launch_gateup_r(const uint16_t* x, int T, const uint8_t* slots, const Geom& g, RouteBufs rb,
+                           DecodeBufs db, int maxA_T, int maxA, const Launch& lc) {
+    static int granted = 64 * 1024;
+    const int xbytes = (T + 1) * (g.H + 8) * 2 + 16;  // + the zero row and the dummy slot of the staging stores
+    const int lds = xbytes > 3 * 4 * 64 * 16 ? xbytes : 3 * 4 * 64 * 16;
+    hipError_t e = ensure_lds(k_gateup_decode<FMT, NC, XPER, R>, lds, granted);
+    if (e != hipSuccess) return e;
+    launch(k_gateup_decode<FMT, NC, XPER, R>, dim3(maxA_T * (g.F / 16)), dim3(256), lds, lc, x, T, slots, g, rb.sx,
+           rb.nact, rb.act, rb.wtab, maxA, db.afrag, db.spart);
+    return hipGetLastError();
 }
 
 template <int FMT, int NC, int XPER>
 hipError_t launch_gateup_x(const uint16_t* x, int T, const uint8_t* slots, const Geom& g, RouteBufs rb,
                            DecodeBufs db, int maxA_T, int maxA, const Launch& lc) {
-    static int granted = 64 * 1024;
-    const int xbytes = (T + 1) * (g.H + 8) * 2 + 16;  // + the zero row and the dummy slot of the staging stores
-    const int lds = xbytes > 3 * 4 * 64 * 16 ? xbytes : 3 * 4 * 64 * 16;
-    hipError_t e = ensure_lds(k_gateup_decode<FMT, NC, XPER>, lds, granted);
-    if (e != hipSuccess) return e;
-    launch(k_gateup_decode<FMT, NC, XPER>, dim3(maxA_T * (g.F / 16)), dim3(256), lds, lc, x, T, slots, g, rb.sx,
-           rb.nact, rb.act, rb.wtab, maxA, db.afrag, db.spart);
-    return hipGetLastError();
+    if (T <= 4) return launch_gateup_r<FMT, NC, XPER, 1>(x, T, slots, g, rb, db, maxA_T, maxA, lc);
+    return launch_gateup_r<FMT, NC, XPER, 2>(x, T, slots, g, rb, db, maxA_T, maxA, lc);
 }
 
 template <int FMT, int NC>
@@ -647,11 +665,13 @@ constexpr int kRing = 8;  // chunks in flight per wave beyond the one being mult
 // Grid (ceil(H/128), min(E, T k) + S), 512 threads.  Workgroup (rg, a)
 // computes the down projection of active expert a for rows 128rg..128rg+127
 // (wave w: row tile 8rg+w).  The workgroup first requests the expert's A
-// fragments (v hi rows 0..7 | v lo rows 8..15), then each wave requests the
+// fragments (token t: v hi in row 4 (t % 4) + 2 (t / 4), v lo in the row
+// after, so a lane's result registers 0, 1 hold token lane / 16 and 2, 3 token
+// lane / 16 + 4; NV = 2 for T <= 4 skips the latter), then each wave requests the
 // first kRing chunks of its row tile; the fragments go to LDS as soon as they
 // arrive and every further chunk is requested as one is consumed.  K = F fits
 // one pass (nch <= NC).  Output: part[a][t][row].
-template <int FMT, int NC, int FPER>
+template <int FMT, int NC, int FPER, int NV>
 __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots, Geom g,
                                                      const int32_t* __restrict__ nact, const int32_t* __restrict__ act,
                                                      int maxA, const uint32_t* __restrict__ afrag,
@@ -699,7 +719,7 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots
 #pragma unroll
         for (int j = 0; j < 4; ++j) A[j] = frag[min(c * 4 + j, nbp - 1) * 64 + lane];
         const u32x2_t scc = c < md.nch ? sc[i] : u32x2_t{0u, 0u};  // padding chunk (NC > nch): zero scales
-        chunk_mac<FMT>(cw[i], scc, A, s0[i] + s1[i], gs, acc, corr);
+        chunk_mac<FMT, NV>(cw[i], scc, A, s0[i] + s1[i], gs, acc, corr);
     };
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -725,30 +745,32 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots
         }
     }
     if (!live) return;
-    f32x4_t v;
+    float v[NV];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = acc[i] - QF<FMT>::kBias * corr[i];
-    f32x4_t other;
+    for (int i = 0; i < NV; ++i) v[i] = acc[i] - QF<FMT>::kBias * corr[i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) other[i] = __shfl_xor(v[i], 32);
-    if (lane < 32) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 4 * gs + i;
-            if (t < T) part[((int64_t)a * kMaxDecodeT + t) * g.H + rt * 16 + n] = v[i] + other[i];
-        }
+    for (int h = 0; h < NV / 2; ++h) {
+        const int t = gs + 4 * h;  // hi + lo
+        if (t < T) part[((int64_t)a * kMaxDecodeT + t) * g.H + rt * 16 + n] = v[2 * h] + v[2 * h + 1];
     }
+}
+
+template <int FMT, int NC, int FPER, int NV>
+hipError_t launch_down_v(int T, const uint8_t* slots, const Geom& g, RouteBufs rb, DecodeBufs db, dim3 grid, int lds,
+                         int maxA, const Launch& lc) {
+    static int granted = 64 * 1024;
+    hipError_t e = ensure_lds(k_down_decode<FMT, NC, FPER, NV>, lds, granted);
+    if (e != hipSuccess) return e;
+    launch(k_down_decode<FMT, NC, FPER, NV>, grid, dim3(512), lds, lc, T, slots, g, rb.nact, rb.act, maxA, db.afrag,
+           db.spart, db.part);
+    return hipGetLastError();
 }
 
 template <int FMT, int NC, int FPER>
 hipError_t launch_down_f(int T, const uint8_t* slots, const Geom& g, RouteBufs rb, DecodeBufs db, dim3 grid, int lds,
                          int maxA, const Launch& lc) {
-    static int granted = 64 * 1024;
-    hipError_t e = ensure_lds(k_down_decode<FMT, NC, FPER>, lds, granted);
-    if (e != hipSuccess) return e;
-    launch(k_down_decode<FMT, NC, FPER>, grid, dim3(512), lds, lc, T, slots, g, rb.nact, rb.act, maxA, db.afrag,
-           db.spart, db.part);
-    return hipGetLastError();
+    if (T <= 4) return launch_down_v<FMT, NC, FPER, 2>(T, slots, g, rb, db, grid, lds, maxA, lc);
+    return launch_down_v<FMT, NC, FPER, 4>(T, slots, g, rb, db, grid, lds, maxA, lc);
 }
 
 template <int FMT, int NC>
