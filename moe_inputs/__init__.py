@@ -9,7 +9,7 @@ import os
 
 import numpy as np
 
-from .configs import (BIAS_NONE, BIAS_NORMAL, BIAS_ZIPF, CONFIGS, Q2B32, Q4B32,  # noqa: F401
+from .configs import (BIAS_NONE, BIAS_NORMAL, BIAS_ZIPF, CONFIGS, Q2B32, Q2B64, Q4B32,  # noqa: F401
                       MoEConfig)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -49,6 +49,8 @@ def lib():
         vp = ctypes.c_void_p
         L.moe_gen_block_bytes.argtypes = [i32]
         L.moe_gen_block_bytes.restype = i64
+        L.moe_gen_block_weights.argtypes = [i32]
+        L.moe_gen_block_weights.restype = i32
         L.moe_gen_expert_bytes.argtypes = [i32, i32, i32]
         L.moe_gen_expert_bytes.restype = i64
         L.moe_gen_quantize_block.argtypes = [vp, i32, vp]
@@ -78,6 +80,10 @@ def block_bytes(fmt: int) -> int:
     return int(lib().moe_gen_block_bytes(fmt))
 
 
+def block_weights(fmt: int) -> int:
+    return int(lib().moe_gen_block_weights(fmt))
+
+
 def normals(seed: int, tag: int, a: int, b: int, start: int, n: int) -> np.ndarray:
     out = np.empty(n, dtype=np.float64)
     lib().moe_gen_normals(seed, tag, a, b, start, n, _ptr(out))
@@ -86,7 +92,7 @@ def normals(seed: int, tag: int, a: int, b: int, start: int, n: int) -> np.ndarr
 
 def quantize_block(w: np.ndarray, fmt: int) -> np.ndarray:
     w = np.ascontiguousarray(w, dtype=np.float64)
-    assert w.shape == (32,)
+    assert w.shape == (block_weights(fmt),)
     out = np.zeros(block_bytes(fmt), dtype=np.uint8)
     lib().moe_gen_quantize_block(_ptr(w), fmt, _ptr(out))
     return out

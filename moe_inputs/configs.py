@@ -21,6 +21,7 @@ from typing import Tuple
 
 Q4B32 = 1
 Q2B32 = 2
+Q2B64 = 3  # 2-bit codes, one fp16 scale per 64 weights: 2.25 bits per weight
 
 BIAS_NONE = 0
 BIAS_ZIPF = 1
@@ -37,7 +38,7 @@ class MoEConfig:
     S: int                  # shared experts (0 or 1)
     k: int                  # top-k
     L: int                  # layers
-    fmt: int                # Q4B32 or Q2B32
+    fmt: int                # Q4B32, Q2B32 or Q2B64
     bias_kind: int
     bias_param: float
     seeds: Tuple[int, ...] = field(default=(1,))
@@ -45,11 +46,15 @@ class MoEConfig:
 
     @property
     def block_bytes(self) -> int:
-        return 18 if self.fmt == Q4B32 else 10
+        return 10 if self.fmt == Q2B32 else 18
+
+    @property
+    def block_weights(self) -> int:
+        return 64 if self.fmt == Q2B64 else 32
 
     @property
     def expert_bytes(self) -> int:
-        return 3 * self.H * self.F // 32 * self.block_bytes
+        return 3 * self.H * self.F // self.block_weights * self.block_bytes
 
     @property
     def router_bytes(self) -> int:
@@ -64,6 +69,13 @@ C3 = MoEConfig("C3", (1, 4, 8), 2560, 640, 512, 0, 10, 48, Q2B32, BIAS_ZIPF, 1.1
                "Qwen-shaped 48-layer decode chain with residual, windows 1/4/8, q2b32, per-layer Zipf(1.1)")
 C4 = MoEConfig("C4", (1, 4, 8), 4096, 2048, 256, 1, 6, 43, Q4B32, BIAS_NORMAL, 0.5, (1, 2, 3),
                "DeepSeek-shaped 43-layer decode chain, 256+1 experts, top-6, FF 2048, q4b32, bias N(0,0.5)")
+# The Qwen-shaped layer and chain with the 2.25-bit expert format (one fp16
+# scale per 64 weights): 1,382,400 bytes per expert, the size of the pages'
+# 2-bit expert blob, and 48 x 512 experts in 33.97 GB.
+C2_Q2B64 = MoEConfig("C2_q2b64", (4,), 2560, 640, 512, 0, 10, 1, Q2B64, BIAS_ZIPF, 1.1, (1, 2, 3),
+                     "Qwen-shaped decode layer as C2 with q2b64 experts (2.25 bits per weight)")
+C3_Q2B64 = MoEConfig("C3_q2b64", (1, 4, 8), 2560, 640, 512, 0, 10, 48, Q2B64, BIAS_ZIPF, 1.1, (1, 2, 3),
+                     "Qwen-shaped 48-layer decode chain as C3 with q2b64 experts (2.25 bits per weight)")
 # Zipf exponent for the prefill chunk: the smallest multiple of 0.1 for which the
 # seed-1 routing (computed by the oracle) sends more than 500 tokens to some
 # expert.  Written by tests/golden/make_golden.py; see tests/golden/c5_zipf.json.
@@ -71,4 +83,4 @@ C5_ZIPF_S = 0.3
 C5 = MoEConfig("C5", (4096,), 4096, 2048, 256, 1, 6, 1, Q4B32, BIAS_ZIPF, C5_ZIPF_S, (1, 2, 3),
                "DeepSeek-shaped prefill chunk: 4096 tokens, 256+1 experts, top-6, FF 2048, q4b32, Zipf-skewed")
 
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5)}
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C2_Q2B64, C3_Q2B64)}

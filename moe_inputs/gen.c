@@ -20,15 +20,17 @@
  * 43 layers, 256 routed + 1 shared, top-6, hidden 4096, FF 2048 -- page
  * "Strata 改源码去跑 DeepSeek V4 Flash？", section 二 GGUF table).
  *
- * Canonical expert format (both formats: blocks of 32 weights along the
- * input dimension of one output row):
+ * Canonical expert format (blocks of BW consecutive weights along the input
+ * dimension of one output row; BW = 32 for q4b32 and q2b32, 64 for q2b64):
  *   expert = G rows [F x H], then U rows [F x H], then D rows [H x F];
- *   each row is K/32 blocks (K = H for G and U, K = F for D);
+ *   each row is K/BW blocks (K = H for G and U, K = F for D);
  *   block  = fp16 scale d (little-endian) followed by the codes;
  *   q4b32: weight j in byte j>>1, low nibble first   (18 bytes per block),
  *          w = d*(q-8);
  *   q2b32: weight j in byte j>>2 at bit 2*(j&3)       (10 bytes per block),
- *          w = d*(q-2).
+ *          w = d*(q-2);
+ *   q2b64: as q2b32 with 64 weights per block          (18 bytes per block,
+ *          2.25 bits per weight: the size of the pages' 2-bit expert blob).
  * Quantiser used to make the codes from N(0, 0.02) draws:
  *   d = fp16_rne(fp32_rne(absmax / qmax)) with qmax = 7 (q4) or 1 (q2);
  *   q = clamp(rne(w/d) + o, 0, 2^bits - 1); if d == 0 every q = o.
@@ -104,21 +106,27 @@ static double f16_bits_value(uint16_t h) {
     return (h & 0x8000u) ? -v : v;
 }
 
-int64_t moe_gen_block_bytes(int32_t fmt) { return fmt == 1 ? 18 : fmt == 2 ? 10 : -1; }
+int64_t moe_gen_block_bytes(int32_t fmt) { return fmt == 1 ? 18 : fmt == 2 ? 10 : fmt == 3 ? 18 : -1; }
+
+/* Weights per block. */
+int32_t moe_gen_block_weights(int32_t fmt) { return fmt == 3 ? 64 : 32; }
 
 int64_t moe_gen_expert_bytes(int32_t H, int32_t F, int32_t fmt) {
     int64_t bb = moe_gen_block_bytes(fmt);
-    if (bb < 0 || H <= 0 || F <= 0 || H % 32 || F % 32) return -1;
-    return 3 * (int64_t)H * F / 32 * bb;
+    const int32_t bw = moe_gen_block_weights(fmt);
+    if (bb < 0 || H <= 0 || F <= 0 || H % bw || F % bw) return -1;
+    return 3 * (int64_t)H * F / bw * bb;
 }
 
-/* Quantise 32 weights into one canonical block (fmt 1 = q4b32, 2 = q2b32). */
+/* Quantise one block of weights (32, or 64 for fmt 3) into canonical bytes
+ * (fmt 1 = q4b32, 2 = q2b32, 3 = q2b64). */
 void moe_gen_quantize_block(const double* w, int32_t fmt, uint8_t* out) {
     const int bits = fmt == 1 ? 4 : 2;
     const double qmax = fmt == 1 ? 7.0 : 1.0;
     const int o = 1 << (bits - 1), nmax = (1 << bits) - 1;
+    const int bw = moe_gen_block_weights(fmt);
     double amax = 0.0;
-    for (int j = 0; j < 32; ++j) {
+    for (int j = 0; j < bw; ++j) {
         double a = fabs(w[j]);
         amax = a > amax ? a : amax;
     }
@@ -126,19 +134,19 @@ void moe_gen_quantize_block(const double* w, int32_t fmt, uint8_t* out) {
     double d = f16_bits_value(d16);
     out[0] = (uint8_t)(d16 & 0xFF);
     out[1] = (uint8_t)(d16 >> 8);
-    int q[32];
+    int q[64];
     if (d != 0.0) {
-        for (int j = 0; j < 32; ++j) {
+        for (int j = 0; j < bw; ++j) {
             double r = nearbyint(w[j] / d) + (double)o;
             q[j] = (int)(r < 0.0 ? 0.0 : r > (double)nmax ? (double)nmax : r);
         }
     } else {
-        for (int j = 0; j < 32; ++j) q[j] = o;
+        for (int j = 0; j < bw; ++j) q[j] = o;
     }
     if (bits == 4)
         for (int j = 0; j < 16; ++j) out[2 + j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
     else
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < bw / 4; ++j)
             out[2 + j] = (uint8_t)(q[4 * j] | (q[4 * j + 1] << 2) | (q[4 * j + 2] << 4) | (q[4 * j + 3] << 6));
 }
 
@@ -201,6 +209,7 @@ void moe_gen_experts(uint64_t seed, uint32_t layer, int32_t e_begin, int32_t cou
     if (per_expert < 0) return;
     const int64_t rows_total = 2 * (int64_t)F + H; /* G rows, U rows, D rows */
     const int bits = fmt == 1 ? 4 : 2;
+    const int64_t bw = moe_gen_block_weights(fmt);
 #pragma omp parallel for schedule(dynamic, 16) collapse(2)
     for (int32_t ei = 0; ei < count; ++ei) {
         for (int64_t row = 0; row < rows_total; ++row) {
@@ -210,26 +219,26 @@ void moe_gen_experts(uint64_t seed, uint32_t layer, int32_t e_begin, int32_t cou
             /* element offset of this row inside the expert: G and U rows have H
              * elements, D rows have F; all three matrices hold F*H elements. */
             const int64_t elem0 = row < 2 * (int64_t)F ? row * H : 2 * (int64_t)F * H + (row - 2 * (int64_t)F) * F;
-            const int64_t byte0 = row < 2 * (int64_t)F ? row * (H / 32) * bb
-                                                      : 2 * (int64_t)F * (H / 32) * bb + (row - 2 * (int64_t)F) * (F / 32) * bb;
+            const int64_t byte0 = row < 2 * (int64_t)F ? row * (H / bw) * bb
+                                                      : 2 * (int64_t)F * (H / bw) * bb + (row - 2 * (int64_t)F) * (F / bw) * bb;
             uint8_t* dst = out + (int64_t)ei * per_expert + byte0;
             if (!raw) {
                 double w[4096];
                 for (int64_t c0 = 0; c0 < K; c0 += 4096) {
                     const int64_t n = K - c0 < 4096 ? K - c0 : 4096;
                     for (int64_t j = 0; j < n; ++j) w[j] = 0.02 * normal_of(draw(key, (uint64_t)(elem0 + c0 + j)));
-                    for (int64_t blk = 0; blk < n / 32; ++blk)
-                        moe_gen_quantize_block(w + blk * 32, fmt, dst + (c0 / 32 + blk) * bb);
+                    for (int64_t blk = 0; blk < n / bw; ++blk)
+                        moe_gen_quantize_block(w + blk * bw, fmt, dst + (c0 / bw + blk) * bb);
                 }
             } else {
-                for (int64_t blk = 0; blk < K / 32; ++blk) {
+                for (int64_t blk = 0; blk < K / bw; ++blk) {
                     uint8_t* o = dst + blk * bb;
-                    uint64_t r0 = draw(key, (uint64_t)(elem0 + blk * 32));
+                    uint64_t r0 = draw(key, (uint64_t)(elem0 + blk * bw));
                     uint16_t d16 = f64_to_f16_rne(0.002 * normal_of(r0));
                     o[0] = (uint8_t)(d16 & 0xFF);
                     o[1] = (uint8_t)(d16 >> 8);
-                    for (int j = 0; j < bits * 4; ++j)
-                        o[2 + j] = (uint8_t)(draw(key, (uint64_t)(elem0 + blk * 32 + 1 + j)) >> 24);
+                    for (int j = 0; j < bits * bw / 8; ++j)
+                        o[2 + j] = (uint8_t)(draw(key, (uint64_t)(elem0 + blk * bw + 1 + j)) >> 24);
                 }
             }
         }

@@ -18,7 +18,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
-Q4B32, Q2B32 = 1, 2
+Q4B32, Q2B32, Q2B64 = 1, 2, 3
 _lib = None
 
 
@@ -106,8 +106,9 @@ def dequant_rows(blocks: np.ndarray, rows: int, K: int, fmt: int) -> np.ndarray:
 
 def expert_matrices(expert: np.ndarray, H: int, F: int, fmt: int):
     """(G [FxH], U [FxH], D [HxF]) dequantised from one expert's canonical bytes."""
-    bb = 18 if fmt == Q4B32 else 10
-    ng = F * (H // 32) * bb
+    bb = 10 if fmt == Q2B32 else 18
+    bw = 64 if fmt == Q2B64 else 32
+    ng = F * (H // bw) * bb
     e = np.ascontiguousarray(expert)
     G = dequant_rows(e[:ng], F, H, fmt)
     U = dequant_rows(e[ng:2 * ng], F, H, fmt)

@@ -35,11 +35,13 @@
  *    shared expert added with weight 1 outside the renormalisation.
  *
  * Inputs are decoded exactly: bf16 and IEEE binary16 bit patterns become
- * doubles, and a block weight is d*(q-o) with o = 8 (q4b32) or 2 (q2b32).
+ * doubles, and a block weight is d*(q-o) with o = 8 (q4b32) or 2 (q2b32,
+ * q2b64).
  * Canonical block layout: fp16 scale d (little-endian), then the codes;
- * q4b32 weight j in byte j>>1 (low nibble first), q2b32 weight j in byte j>>2
- * at bit 2*(j&3).  An expert is its G rows [F x H], then U rows [F x H], then
- * D rows [H x F], each row K/32 blocks along its input dimension.
+ * q4b32 weight j in byte j>>1 (low nibble first), q2b32 and q2b64 weight j in
+ * byte j>>2 at bit 2*(j&3).  An expert is its G rows [F x H], then U rows
+ * [F x H], then D rows [H x F], each row K/BW blocks along its input dimension
+ * (BW = 32, or 64 for q2b64).
  */
 #include <math.h>
 #include <stdint.h>
@@ -49,6 +51,7 @@
 
 #define ORACLE_Q4B32 1
 #define ORACLE_Q2B32 2
+#define ORACLE_Q2B64 3
 
 /* bf16 bit pattern -> double (exact). */
 double oracle_bf16(uint16_t b) {
@@ -70,9 +73,17 @@ double oracle_fp16(uint16_t h) {
     return (h & 0x8000) ? -v : v;
 }
 
-int64_t oracle_block_bytes(int fmt) { return fmt == ORACLE_Q4B32 ? 18 : fmt == ORACLE_Q2B32 ? 10 : -1; }
+int64_t oracle_block_bytes(int fmt) {
+    return fmt == ORACLE_Q4B32 ? 18 : fmt == ORACLE_Q2B32 ? 10 : fmt == ORACLE_Q2B64 ? 18 : -1;
+}
 
-/* Weight j (0..31) of one canonical block. */
+/* Weights per block: 32, or 64 for q2b64 (one fp16 scale per 64 two-bit
+ * codes, 2.25 bits per weight: the size of the 2-bit expert blob in the
+ * teardown page "Strata 引擎深度拆解", section 二, 1,382,400 bytes per
+ * 2560 x 640 expert, and of its 34 GB expert total). */
+int oracle_block_weights(int fmt) { return fmt == ORACLE_Q2B64 ? 64 : 32; }
+
+/* Weight j (0..31, or 0..63 for q2b64) of one canonical block. */
 double oracle_block_weight(const uint8_t* blk, int fmt, int j) {
     double d = oracle_fp16((uint16_t)(blk[0] | (blk[1] << 8)));
     int q, o;
@@ -89,26 +100,29 @@ double oracle_block_weight(const uint8_t* blk, int fmt, int j) {
 /* Dequantise a [rows x K] matrix stored as canonical blocks. */
 void oracle_dequant_rows(const uint8_t* blocks, int rows, int K, int fmt, double* out) {
     const int64_t bb = oracle_block_bytes(fmt);
+    const int bw = oracle_block_weights(fmt);
     for (int r = 0; r < rows; ++r)
         for (int c = 0; c < K; ++c)
-            out[(int64_t)r * K + c] = oracle_block_weight(blocks + ((int64_t)r * (K / 32) + c / 32) * bb, fmt, c % 32);
+            out[(int64_t)r * K + c] = oracle_block_weight(blocks + ((int64_t)r * (K / bw) + c / bw) * bb, fmt, c % bw);
 }
 
 /* Byte offsets of the three matrices inside one expert. */
 static void expert_parts(int H, int F, int fmt, int64_t* g, int64_t* u, int64_t* d) {
     const int64_t bb = oracle_block_bytes(fmt);
+    const int bw = oracle_block_weights(fmt);
     *g = 0;
-    *u = (int64_t)F * (H / 32) * bb;
-    *d = 2 * (int64_t)F * (H / 32) * bb;
+    *u = (int64_t)F * (H / bw) * bb;
+    *d = 2 * (int64_t)F * (H / bw) * bb;
 }
 
 /* y = M v for M [rows x K] in canonical blocks; sum in column order. */
 static void matvec(const uint8_t* blocks, int rows, int K, int fmt, const double* v, double* y) {
     const int64_t bb = oracle_block_bytes(fmt);
+    const int bw = oracle_block_weights(fmt);
     for (int r = 0; r < rows; ++r) {
         double s = 0.0;
         for (int c = 0; c < K; ++c)
-            s += oracle_block_weight(blocks + ((int64_t)r * (K / 32) + c / 32) * bb, fmt, c % 32) * v[c];
+            s += oracle_block_weight(blocks + ((int64_t)r * (K / bw) + c / bw) * bb, fmt, c % bw) * v[c];
         y[r] = s;
     }
 }

@@ -15,7 +15,7 @@ import torch
 
 import moe_inputs as mi
 import oracle
-from moe_inputs.configs import C1, C2, C3, C4, C5, CONFIGS, Q2B32, Q4B32
+from moe_inputs.configs import C1, C2, C2_Q2B64, C3, C3_Q2B64, C4, C5, CONFIGS, Q2B32, Q2B64, Q4B32
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -40,6 +40,10 @@ def test_bf16_decode_matches_torch_all_patterns():
     assert np.array_equal(got[finite], ref[finite])
 
 
+ALL_FMTS = [Q4B32, Q2B32, Q2B64]
+BW = {Q4B32: 32, Q2B32: 32, Q2B64: 64}  # weights per block
+
+
 def _numpy_decode_block(block: np.ndarray, fmt: int) -> np.ndarray:
     """Independent numpy decoder of one canonical block (bit unpacking by numpy)."""
     d = float(block[:2].view(np.float16)[0])
@@ -51,46 +55,66 @@ def _numpy_decode_block(block: np.ndarray, fmt: int) -> np.ndarray:
     return d * (q - 2)
 
 
-@pytest.mark.parametrize("fmt", [Q4B32, Q2B32])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_block_decode_matches_numpy_decoder(fmt):
     ex = mi.gen_experts(7, 0, 0, 1, 256, 128, fmt, raw=True)
     bb = mi.block_bytes(fmt)
+    assert mi.block_weights(fmt) == BW[fmt]
     blocks = ex.reshape(-1, bb)[:200]
     for blk in blocks:
         ref = _numpy_decode_block(blk, fmt)
-        got = np.array([oracle.block_weight(blk, fmt, j) for j in range(32)])
+        assert ref.shape == (BW[fmt],)
+        got = np.array([oracle.block_weight(blk, fmt, j) for j in range(BW[fmt])])
         np.testing.assert_array_equal(got, ref)
 
 
-@pytest.mark.parametrize("fmt", [Q4B32, Q2B32])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+def test_matrix_decode_matches_numpy_decoder(fmt):
+    """Whole G, U and D of one expert: row r, column c is element c % BW of
+    block r * (K / BW) + c / BW of its matrix (numpy reshape, no oracle indexing)."""
+    H, F = 256, 128
+    ex = mi.gen_experts(8, 0, 0, 1, H, F, fmt, raw=True)
+    bb, bw = mi.block_bytes(fmt), BW[fmt]
+    blocks = ex.reshape(-1, bb)
+    dec = np.stack([_numpy_decode_block(b, fmt) for b in blocks])  # [nblocks x bw]
+    ng = F * H // bw
+    G, U, D = oracle.expert_matrices(ex, H, F, fmt)
+    np.testing.assert_array_equal(G, dec[:ng].reshape(F, H))
+    np.testing.assert_array_equal(U, dec[ng:2 * ng].reshape(F, H))
+    np.testing.assert_array_equal(D, dec[2 * ng:].reshape(H, F))
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_dequant_round_trip_on_grid(fmt):
     """Weights on the grid d*(q-o) re-quantise to identical bytes."""
     rng = np.random.default_rng(3)
     nq = 16 if fmt == Q4B32 else 4
     o = 8 if fmt == Q4B32 else 2
     qmax = 7 if fmt == Q4B32 else 1
+    bw = BW[fmt]
     for _ in range(200):
-        q = rng.integers(0, nq, size=32)
-        q[rng.integers(0, 32)] = o + qmax  # the block's absmax sits on code o+qmax
+        q = rng.integers(0, nq, size=bw)
+        q[rng.integers(0, bw)] = o + qmax  # the block's absmax sits on code o+qmax
         q = np.where(np.abs(q - o) > qmax, o + qmax, q)
         d = float(np.float16(rng.uniform(1e-4, 1e-1)))
         w = d * (q - o).astype(np.float64)
         blk = mi.quantize_block(w, fmt)
-        deq = np.array([oracle.block_weight(blk, fmt, j) for j in range(32)])
+        deq = np.array([oracle.block_weight(blk, fmt, j) for j in range(bw)])
         np.testing.assert_array_equal(deq, w)
         np.testing.assert_array_equal(mi.quantize_block(deq, fmt), blk)
 
 
-@pytest.mark.parametrize("fmt", [Q4B32, Q2B32])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_dequant_error_bound_off_grid(fmt):
     """Quantised N(0,0.02) draws decode within d/2 of the draw (no clamping
     inside the scale's range)."""
     qmax = 7 if fmt == Q4B32 else 1
-    z = mi.normals(11, mi.TAG_EXPERT, 0, 0, 0, 32 * 300).reshape(300, 32) * 0.02
+    bw = BW[fmt]
+    z = mi.normals(11, mi.TAG_EXPERT, 0, 0, 0, bw * 300).reshape(300, bw) * 0.02
     for w in z:
         blk = mi.quantize_block(w, fmt)
         d = oracle.fp16_value(int(blk[0]) | (int(blk[1]) << 8))
-        deq = np.array([oracle.block_weight(blk, fmt, j) for j in range(32)])
+        deq = np.array([oracle.block_weight(blk, fmt, j) for j in range(bw)])
         amax = np.abs(w).max()
         inside = np.abs(w) <= d * qmax
         assert np.all(np.abs(w - deq)[inside] <= d / 2 + 1e-15)
@@ -256,15 +280,15 @@ def _dense_ffn(G, U, D, x):
     return D @ (g * scipy.special.expit(g) * u)
 
 
-@pytest.mark.parametrize("fmt", [Q4B32, Q2B32])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_single_expert_equals_dense_ffn(fmt):
     """E = 1, k = 1: the layer is one dense FFN (numpy float64 matmuls)."""
-    H, F = 256, 96
+    H, F = 256, 96 if BW[fmt] == 32 else 128
     ex = mi.gen_experts(4, 0, 0, 1, H, F, fmt)
     G, U, D = oracle.expert_matrices(ex, H, F, fmt)
     # the matrices decode the same through the independent numpy decoder
     bb = mi.block_bytes(fmt)
-    np.testing.assert_array_equal(G.ravel()[:32], _numpy_decode_block(ex[:bb], fmt))
+    np.testing.assert_array_equal(G.ravel()[:BW[fmt]], _numpy_decode_block(ex[:bb], fmt))
     x = mi.gen_x(4, 0, 3, H)
     W = mi.gen_router(4, 0, 1, H)
     y, ids, w, _ = oracle.moe_layer(x, H, F, 1, 0, 1, fmt, W, None, ex, len(ex))
@@ -383,6 +407,11 @@ def test_byte_accounting_matches_pages():
     assert C2.expert_bytes == 1_536_000 == 1_382_400 * 10 // 9
     # "about 700 more experts per GB" of the 2.25-bit blob
     assert int(1e9 // 1_382_400) == 723
+    # q2b64 (one fp16 scale per 64 two-bit codes) is exactly the blob, and the
+    # 48 x 512 Qwen experts take the pages' "34 GB"
+    assert C2_Q2B64.expert_bytes == C3_Q2B64.expert_bytes == 1_382_400
+    assert mi.expert_bytes(2560, 640, Q2B64) == 1_382_400
+    assert round(48 * 512 * C3_Q2B64.expert_bytes / 1e9) == 34
 
 
 def test_c5_zipf_calibration_fixture():
