@@ -18,6 +18,9 @@ prefill chunk (4096 tokens x hidden 4096, 256+1 experts, top-6, FF 2048,
 q4b32, Zipf-skewed routing): a step is one moe_forward of the whole chunk,
 and the roofline is that of the gate/up grouped GEMM on bf16 MFMA.
 
+C2_q2b64 and C3_q2b64 are C2 and C3 with q2b64 experts (one fp16 scale per
+64 2-bit codes: 2.25 bits per weight, 1,382,400 bytes per expert).
+
 Timed steps replay a HIP graph of one input cycle (the eager time of the same
 steps is reported as ms_per_step_eager).
 
@@ -51,7 +54,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=960)
     p.add_argument("--warmup", type=int, default=96)
-    p.add_argument("--workload", default="C2", choices=["C2", "C3", "C4", "C5"])
+    p.add_argument("--workload", default="C2", choices=["C2", "C3", "C4", "C5", "C2_q2b64", "C3_q2b64"])
     p.add_argument("--T", type=int, default=4, help="tokens per window")
     p.add_argument("--layers", type=int, default=0, help="resident layers (default: 48 for C2/C3, 43 for C4)")
     p.add_argument("--windows", type=int, default=16)
@@ -79,13 +82,13 @@ def main():
     import torch
 
     import moe_inputs as mi
-    from moe_inputs.configs import C2, C3, C4
+    from moe_inputs.configs import C2, C2_Q2B64, C3, C3_Q2B64, C4
     from quantized_expert_ffn_softmax_amd import MoEContext
 
-    cfg = {"C2": C2, "C3": C3, "C4": C4}[args.workload]
+    cfg = {"C2": C2, "C3": C3, "C4": C4, "C2_q2b64": C2_Q2B64, "C3_q2b64": C3_Q2B64}[args.workload]
     L = args.layers or (43 if args.workload == "C4" else 48)
     T = args.T
-    chain = args.workload in ("C3", "C4")
+    chain = args.workload in ("C3", "C4", "C3_q2b64")
     torch.cuda.init()
     dev = torch.device("cuda:0")
 
@@ -244,7 +247,7 @@ def main():
                                                   f"{L} resident layers and {len(xs)} windows" if not chain else
                                                   f"{L}-layer MoE-only decode chain with residual per step")),
             "T": T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "S": cfg.S, "k": cfg.k, "layers_resident": L,
-            "quant": "q4b32" if cfg.fmt == 1 else "q2b32", "seed": args.seed,
+            "quant": {1: "q4b32", 2: "q2b32", 3: "q2b64"}[cfg.fmt], "seed": args.seed,
             "launch": f"HIP graph replay of {cycle}-step cycles",
         },
         "hbm_GBps": round(hbm_gbps, 1),

@@ -28,11 +28,16 @@
  *
  * Expert byte format accepted by moe_load_experts ("canonical blocks"): an
  * expert is G rows, then U rows, then D rows; every row is a sequence of
- * blocks of 32 consecutive weights along its input dimension; a block is an
+ * blocks of BW consecutive weights along its input dimension; a block is an
  * fp16 scale d (little-endian) followed by the codes:
- *   MOE_Q4B32  18 bytes/block, weight j in byte j>>1 (low nibble first), w = d*(q-8)
- *   MOE_Q2B32  10 bytes/block, weight j in byte j>>2 at bit 2*(j&3),     w = d*(q-2)
- * so one expert is 3*H*F/32 blocks (q4b32 at H=4096, F=2048: 14,155,776 bytes).
+ *   MOE_Q4B32  BW 32, 18 bytes/block, weight j in byte j>>1 (low nibble first), w = d*(q-8)
+ *   MOE_Q2B32  BW 32, 10 bytes/block, weight j in byte j>>2 at bit 2*(j&3),     w = d*(q-2)
+ *   MOE_Q2B64  BW 64, 18 bytes/block, weight j in byte j>>2 at bit 2*(j&3),     w = d*(q-2)
+ * so one expert is 3*H*F/BW blocks (q4b32 at H=4096, F=2048: 14,155,776 bytes).
+ * MOE_Q2B64 spends 2.25 bits per weight: 1,382,400 bytes per 2560 x 640
+ * expert, the size of the 2-bit expert blob of the teardown page "Strata
+ * 引擎深度拆解", section 二 (which does not print its layout; one fp16 scale
+ * per 64 codes is the reading taken).
  *
  * Conventions for every call:
  *  - Device pointers are plain device addresses on the context's device,
@@ -71,16 +76,17 @@ typedef enum {
     MOE_ERANGE = -5  /* T larger than the context's max_tokens */
 } moe_status;
 
-typedef enum { MOE_Q4B32 = 1, MOE_Q2B32 = 2 } moe_quant;
+typedef enum { MOE_Q4B32 = 1, MOE_Q2B32 = 2, MOE_Q2B64 = 3 } moe_quant;
 
 /* Layer geometry, fixed for the lifetime of a context (E and k are runtime
  * values, as the pages' engine reads them from the model file).
- *   hidden, ffn : H and F, positive multiples of 32, H <= 4096, F <= 2048
+ *   hidden, ffn : H and F, positive multiples of 32 (of 64 for MOE_Q2B64),
+ *                 H <= 4096, F <= 2048
  *   n_experts   : E routed experts, 1..1024
  *   n_shared    : 0 or 1 always-on shared expert (expert index E)
  *   top_k       : k in [1, min(E, 16)]
  *   n_layers    : L >= 1; every layer has its own router and experts
- *   quant       : MOE_Q4B32 or MOE_Q2B32
+ *   quant       : MOE_Q4B32, MOE_Q2B32 or MOE_Q2B64
  *   max_tokens  : largest T accepted by moe_route/moe_forward (1..65536);
  *                 scratch memory is sized for it
  *   device      : HIP device ordinal */
@@ -95,7 +101,8 @@ typedef struct {
  *   experts     : expert_count experts in canonical blocks, experts
  *                 [expert_begin, expert_begin + expert_count); index E is the
  *                 shared expert.  NULL with expert_count = 0 uploads none.
- *   experts_bytes must equal expert_count * 3*H*F/32 * (18 or 10).
+ *   experts_bytes must equal expert_count * moe_expert_bytes(H, F, quant)
+ *                 (3*H*F/32 * 18, 3*H*F/32 * 10 or 3*H*F/64 * 18).
  *   tid2eid     : NULL to leave the layer's routing as is, or a [vocab x k]
  *                 int32 table (vocab >= 1, ids in [0, E), distinct within a
  *                 row) that makes the layer hash-routed from this upload on:

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_ESTATE, MOE_ERANGE = 0, -1, -2, -3, -4, -5
-MOE_Q4B32, MOE_Q2B32 = 1, 2
+MOE_Q4B32, MOE_Q2B32, MOE_Q2B64 = 1, 2, 3
 MOE_FWD_RESIDUAL = 1
 MOE_FWD_PROFILE = 2
 MOE_FWD_PRENORM = 4

@@ -127,7 +127,10 @@ moe_status check_config(const moe_config* cfg) {
     if (cfg->top_k < 1 || cfg->top_k > std::min(cfg->n_experts, kMaxTopK))
         return fail(MOE_EINVAL, "top_k %d outside [1, min(E, %d)]", cfg->top_k, kMaxTopK);
     if (cfg->n_layers < 1 || cfg->n_layers > 4096) return fail(MOE_EINVAL, "n_layers %d outside [1, 4096]", cfg->n_layers);
-    if (cfg->quant != MOE_Q4B32 && cfg->quant != MOE_Q2B32) return fail(MOE_EINVAL, "unknown quant %d", cfg->quant);
+    if (cfg->quant != MOE_Q4B32 && cfg->quant != MOE_Q2B32 && cfg->quant != MOE_Q2B64)
+        return fail(MOE_EINVAL, "unknown quant %d", cfg->quant);
+    if (cfg->quant == MOE_Q2B64 && (cfg->hidden % 64 || cfg->ffn % 64))
+        return fail(MOE_EINVAL, "q2b64: hidden (%d) and ffn (%d) must be multiples of 64", cfg->hidden, cfg->ffn);
     if (cfg->max_tokens < 1 || cfg->max_tokens > 65536)
         return fail(MOE_EINVAL, "max_tokens %d outside [1, 65536]", cfg->max_tokens);
     int ndev = 0;
@@ -154,8 +157,10 @@ extern "C" {
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 int64_t moe_expert_bytes(int32_t hidden, int32_t ffn, int32_t quant) {
-    if (hidden <= 0 || ffn <= 0 || hidden % 32 || ffn % 32 || (quant != MOE_Q4B32 && quant != MOE_Q2B32)) return -1;
-    return 3LL * hidden * ffn / 32 * (quant == MOE_Q4B32 ? 18 : 10);
+    if (quant != MOE_Q4B32 && quant != MOE_Q2B32 && quant != MOE_Q2B64) return -1;
+    const int bw = canon_block_weights(quant);
+    if (hidden <= 0 || ffn <= 0 || hidden % bw || ffn % bw) return -1;
+    return 3LL * hidden * ffn / bw * canon_block_bytes(quant);
 }
 
 moe_status moe_create(const moe_config* cfg, moe_ctx** out) {

@@ -52,6 +52,8 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 template <int FMT> struct QF;
 template <> struct QF<1> { static constexpr float kBias = 136.0f; static constexpr int kCW = 16; };
 template <> struct QF<2> { static constexpr float kBias = 130.0f; static constexpr int kCW = 8; };
+// q2b64: q2 codes, one scale per 64 weights (two consecutive 32-blocks share it)
+template <> struct QF<3> { static constexpr float kBias = 130.0f; static constexpr int kCW = 8; };
 
 // The exponent bits 0x4300 of both bf16 halves, held in a VGPR.  The asm
 // only materialises the constant: as an opaque register value it lets each
@@ -82,6 +84,9 @@ template <> __device__ __forceinline__ u32x4_t unpack<2>(const uint32_t* cw, int
     r.w = ((w >> 6) & 0x00030003u) | k;
     return r;
 }
+template <> __device__ __forceinline__ u32x4_t unpack<3>(const uint32_t* cw, int j, uint32_t k) {
+    return unpack<2>(cw, j, k);
+}
 
 template <int FMT> __device__ __forceinline__ void load_codes(const uint8_t* chunk, int lane, uint32_t* cw) {
     if constexpr (FMT == 1) {
@@ -92,10 +97,16 @@ template <int FMT> __device__ __forceinline__ void load_codes(const uint8_t* chu
         cw[0] = v.x; cw[1] = v.y;
     }
 }
-__device__ __forceinline__ u32x2_t load_scales(const uint8_t* chunk, int cw_bytes, int n) {
-    return *reinterpret_cast<const u32x2_t*>(chunk + 64 * cw_bytes + n * 8);
+// Row n's chunk scales: four fp16 (blocks 0..3), or for q2b64 two fp16 in .x
+// (block j of 32 weights takes the scale of 64-block j / 2).
+template <int FMT> __device__ __forceinline__ u32x2_t load_scales(const uint8_t* chunk, int n) {
+    if constexpr (FMT == 3)
+        return u32x2_t{*reinterpret_cast<const uint32_t*>(chunk + 64 * QF<FMT>::kCW + n * 4), 0u};
+    else
+        return *reinterpret_cast<const u32x2_t*>(chunk + 64 * QF<FMT>::kCW + n * 8);
 }
-__device__ __forceinline__ float scale_of(u32x2_t s, int j) {
+template <int FMT> __device__ __forceinline__ float scale_of(u32x2_t s, int j) {
+    if constexpr (FMT == 3) return h2f((j & 2) ? (s.x >> 16) : (s.x & 0xFFFFu));
     const uint32_t w = (j & 2) ? s.y : s.x;
     return h2f((j & 1) ? (w >> 16) : (w & 0xFFFFu));
 }

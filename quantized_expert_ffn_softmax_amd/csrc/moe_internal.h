@@ -16,7 +16,10 @@
 //           q2 (CW = 8):  word j = blocks 2j (bits 0..7, 16..23) and 2j+1
 //                          (bits 8..15, 24..31); inside a block half, bits 2p
 //                          hold element 8g+2p and bits 16+2p element 8g+2p+1
-//   scales: 16 rows x 4 fp16, row n's scales of blocks 0..3 (8 bytes)
+//           q2b64 codes: as q2 (a 64-weight block is two 32-weight halves)
+//   scales: 16 rows x 4 fp16, row n's scales of blocks 0..3 (8 bytes);
+//           q2b64: 16 rows x 2 fp16, row n's scales of its two 64-blocks
+//           (4 bytes), so a q2b64 chunk is 576 bytes against q2's 640
 //
 // With that bit order, (word >> s) & mask | 0x4300 0x4300 is the bf16 pair
 // (128 + q_k, 128 + q_k+1) for consecutive k, so a code is turned into an
@@ -43,7 +46,7 @@ struct MatGeom {
     int K;           // input dim
     int nb;          // K / 32
     int nch;         // chunks per row tile (nb padded to a multiple of 4, / 4)
-    int chunk_bytes; // q4: 1152, q2: 640
+    int chunk_bytes; // q4: 1152, q2: 640, q2b64: 576
     int64_t tile_bytes;
     int64_t bytes;   // rows/16 * tile_bytes
 };
@@ -58,6 +61,9 @@ struct Geom {
 };
 
 inline int code_bytes_per_lane(int fmt) { return fmt == 1 ? 16 : 8; }
+inline int scale_bytes_per_row(int fmt) { return fmt == 3 ? 4 : 8; }  // per chunk
+inline int canon_block_weights(int fmt) { return fmt == 3 ? 64 : 32; }
+inline int canon_block_bytes(int fmt) { return fmt == 2 ? 10 : 18; }
 
 inline MatGeom make_mat(int rows, int K, int fmt) {
     MatGeom m;
@@ -65,7 +71,7 @@ inline MatGeom make_mat(int rows, int K, int fmt) {
     m.K = K;
     m.nb = K / 32;
     m.nch = (m.nb + kChunkBlocks - 1) / kChunkBlocks;
-    m.chunk_bytes = 64 * code_bytes_per_lane(fmt) + 16 * kChunkBlocks * 2;
+    m.chunk_bytes = 64 * code_bytes_per_lane(fmt) + 16 * scale_bytes_per_row(fmt);
     m.tile_bytes = (int64_t)m.nch * m.chunk_bytes;
     m.bytes = (int64_t)(rows / 16) * m.tile_bytes;
     return m;
@@ -80,7 +86,7 @@ inline Geom make_geom(int H, int F, int E, int S, int k, int fmt, int L) {
     g.u_off = g.gu.bytes;
     g.d_off = 2 * g.gu.bytes;
     g.slot_bytes = (2 * g.gu.bytes + g.dn.bytes + 255) / 256 * 256;
-    g.canon_expert_bytes = 3LL * H * F / 32 * (fmt == 1 ? 18 : 10);
+    g.canon_expert_bytes = 3LL * H * F / canon_block_weights(fmt) * canon_block_bytes(fmt);
     return g;
 }
 

@@ -41,18 +41,31 @@ namespace moe {
 // Only the first NV result registers are scaled and accumulated (a lane's
 // register i holds output row 4 (lane / 16) + i; callers that leave rows
 // 4 g + i, i >= NV, zero need only NV of them).
+// q2b64: the two 32-weight halves of a 64-block share one scale, so their
+// products are summed by the MFMA and scaled once.
 template <int FMT, int NV = 4>
 __device__ __forceinline__ void chunk_mac(const uint32_t* cw, u32x2_t sc, const u32x4_t* A, float s_corr, int g,
                                          f32x4_t& acc, f32x4_t& corr) {
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (FMT == 3) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        f32x4_t R = mfma_bf16(A[j], unpack<FMT>(cw, j, bf16_bias_bits()), zero);
-        const float d = scale_of(sc, j);
+        for (int h = 0; h < 2; ++h) {
+            f32x4_t R = mfma_bf16(A[2 * h], unpack<FMT>(cw, 2 * h, bf16_bias_bits()), zero);
+            R = mfma_bf16(A[2 * h + 1], unpack<FMT>(cw, 2 * h + 1, bf16_bias_bits()), R);
+            const float d = scale_of<FMT>(sc, 2 * h);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) acc[i] += d * R[i];
+            for (int i = 0; i < NV; ++i) acc[i] += d * R[i];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f32x4_t R = mfma_bf16(A[j], unpack<FMT>(cw, j, bf16_bias_bits()), zero);
+            const float d = scale_of<FMT>(sc, j);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) acc[i] += d * R[i];
+        }
     }
-    corr = mfma_f32(s_corr, scale_of(sc, g), corr);
+    corr = mfma_f32(s_corr, scale_of<FMT>(sc, g), corr);
 }
 
 // ---------------------------------------------------------------- repack
@@ -69,18 +82,20 @@ __global__ __launch_bounds__(256) void k_repack(const uint8_t* __restrict__ cano
     const int rt = mat == 0 ? rt_all : mat == 1 ? rt_all - rtF : rt_all - 2 * rtF;
     const MatGeom& m = mat == 2 ? g.dn : g.gu;
     if (c >= m.nch) return;
-    const int bb = g.fmt == 1 ? 18 : 10;
-    const uint8_t* src = canon + (int64_t)ex * g.canon_expert_bytes +
-                         (mat == 0 ? 0 : mat == 1 ? (int64_t)g.F * (g.H / 32) * bb : 2LL * g.F * (g.H / 32) * bb);
+    const int bb = g.fmt == 2 ? 10 : 18;              // canonical block bytes
+    const int bsh = g.fmt == 3 ? 1 : 0;               // log2(canonical block weights / 32)
+    const int64_t gu_bytes = (int64_t)g.F * (g.H / 32 >> bsh) * bb;
+    const uint8_t* src = canon + (int64_t)ex * g.canon_expert_bytes + (mat == 0 ? 0 : mat == 1 ? gu_bytes : 2 * gu_bytes);
     uint8_t* dst = slots + (int64_t)ex * g.slot_bytes + (mat == 0 ? g.g_off : mat == 1 ? g.u_off : g.d_off) +
                    (int64_t)rt * m.tile_bytes + (int64_t)c * m.chunk_bytes;
     const int n = lane & 15, gs = lane >> 4;
     const int row = rt * 16 + n;
     const int o = g.fmt == 1 ? 8 : 2;
-    auto code = [&](int b, int e) -> uint32_t {  // element e of block b of this row
+    auto code = [&](int b, int e) -> uint32_t {  // element e of 32-block b of this row
         if (b >= m.nb) return (uint32_t)o;
-        const uint8_t* blk = src + ((int64_t)row * m.nb + b) * bb + 2;
-        return g.fmt == 1 ? (blk[e >> 1] >> (4 * (e & 1))) & 0xFu : (blk[e >> 2] >> (2 * (e & 3))) & 0x3u;
+        const int ec = e + ((b & bsh) << 5);      // element inside the canonical block
+        const uint8_t* blk = src + ((int64_t)row * (m.nb >> bsh) + (b >> bsh)) * bb + 2;
+        return g.fmt == 1 ? (blk[ec >> 1] >> (4 * (ec & 1))) & 0xFu : (blk[ec >> 2] >> (2 * (ec & 3))) & 0x3u;
     };
     if (g.fmt == 1) {
         uint32_t w[4];
@@ -106,18 +121,24 @@ __global__ __launch_bounds__(256) void k_repack(const uint8_t* __restrict__ cano
         *reinterpret_cast<u32x2_t*>(dst + lane * 8) = u32x2_t{w[0], w[1]};
     }
     if (gs == 0) {
+        // scales of the chunk's canonical blocks (4, or 2 for q2b64); padding blocks get 0
+        const int nsc = 4 >> bsh;
         uint16_t s[4];
-        for (int j = 0; j < 4; ++j) {
-            const int b = c * 4 + j;
-            if (b < m.nb) {
-                const uint8_t* blk = src + ((int64_t)row * m.nb + b) * bb;
+        for (int j = 0; j < nsc; ++j) {
+            const int b = c * nsc + j;
+            if (b < (m.nb >> bsh)) {
+                const uint8_t* blk = src + ((int64_t)row * (m.nb >> bsh) + b) * bb;
                 s[j] = (uint16_t)(blk[0] | (blk[1] << 8));
             } else {
                 s[j] = 0;
             }
         }
-        *reinterpret_cast<u32x2_t*>(dst + 64 * (g.fmt == 1 ? 16 : 8) + n * 8) =
-            u32x2_t{(uint32_t)s[0] | ((uint32_t)s[1] << 16), (uint32_t)s[2] | ((uint32_t)s[3] << 16)};
+        uint8_t* sdst = dst + 64 * (g.fmt == 1 ? 16 : 8);
+        if (g.fmt == 3)
+            *reinterpret_cast<uint32_t*>(sdst + n * 4) = (uint32_t)s[0] | ((uint32_t)s[1] << 16);
+        else
+            *reinterpret_cast<u32x2_t*>(sdst + n * 8) =
+                u32x2_t{(uint32_t)s[0] | ((uint32_t)s[1] << 16), (uint32_t)s[2] | ((uint32_t)s[3] << 16)};
     }
 }
 
@@ -507,9 +528,9 @@ __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restric
         const int c = min(c0 + j, mg.nch - 1);
         const int64_t off = (int64_t)c * mg.chunk_bytes;
         load_codes<FMT>(Gt + off, lane, cg[j]);
-        sg[j] = load_scales(Gt + off, QF<FMT>::kCW, n);
+        sg[j] = load_scales<FMT>(Gt + off, n);
         load_codes<FMT>(Ut + off, lane, cu[j]);
-        su[j] = load_scales(Ut + off, QF<FMT>::kCW, n);
+        su[j] = load_scales<FMT>(Ut + off, n);
         __builtin_amdgcn_sched_barrier(0);
     }
     // routing weights of this lane's tokens R gs + i (used by wave 0 in the epilogue)
@@ -654,6 +675,10 @@ hipError_t launch_gateup_decode(const uint16_t* x, int T, const uint8_t* layer_s
         MOE_GATEUP_CASE(1, 2) MOE_GATEUP_CASE(1, 3) MOE_GATEUP_CASE(1, 4) MOE_GATEUP_CASE(1, 5)
         MOE_GATEUP_CASE(1, 6) return launch_gateup_nc<1, 8>(x, T, layer_slots, g, rb, db, maxA_T, maxA, lc);
     }
+    if (g.fmt == 3) {
+        MOE_GATEUP_CASE(3, 2) MOE_GATEUP_CASE(3, 3) MOE_GATEUP_CASE(3, 4) MOE_GATEUP_CASE(3, 5)
+        MOE_GATEUP_CASE(3, 6) return launch_gateup_nc<3, 8>(x, T, layer_slots, g, rb, db, maxA_T, maxA, lc);
+    }
     MOE_GATEUP_CASE(2, 2) MOE_GATEUP_CASE(2, 3) MOE_GATEUP_CASE(2, 4) MOE_GATEUP_CASE(2, 5)
     MOE_GATEUP_CASE(2, 6) return launch_gateup_nc<2, 8>(x, T, layer_slots, g, rb, db, maxA_T, maxA, lc);
 #undef MOE_GATEUP_CASE
@@ -709,7 +734,7 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots
         s0[i] = sp[bq * 32 + m];
         s1[i] = sp[bq * 32 + 16 + m];
         load_codes<FMT>(Dt + off, lane, cw[i]);
-        sc[i] = load_scales(Dt + off, QF<FMT>::kCW, n);
+        sc[i] = load_scales<FMT>(Dt + off, n);
     };
     // The fragments of all 8 token rows (zeros for t >= T) and of the padded
     // blocks (zeros, never written) are defined, so nothing is masked; chunks
@@ -793,6 +818,10 @@ hipError_t launch_down_decode(int T, const uint8_t* layer_slots, const Geom& g, 
     if (g.fmt == 1) {
         MOE_DOWN_CASE(1, 2) MOE_DOWN_CASE(1, 4) MOE_DOWN_CASE(1, 5) MOE_DOWN_CASE(1, 8)
         return launch_down_nc<1, 16>(T, layer_slots, g, rb, db, grid, lds, maxA, lc);
+    }
+    if (g.fmt == 3) {
+        MOE_DOWN_CASE(3, 2) MOE_DOWN_CASE(3, 4) MOE_DOWN_CASE(3, 5) MOE_DOWN_CASE(3, 8)
+        return launch_down_nc<3, 16>(T, layer_slots, g, rb, db, grid, lds, maxA, lc);
     }
     MOE_DOWN_CASE(2, 2) MOE_DOWN_CASE(2, 4) MOE_DOWN_CASE(2, 5) MOE_DOWN_CASE(2, 8)
     return launch_down_nc<2, 16>(T, layer_slots, g, rb, db, grid, lds, maxA, lc);

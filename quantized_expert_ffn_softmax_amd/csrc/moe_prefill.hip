@@ -471,6 +471,7 @@ __device__ __forceinline__ bool pf_item(int ntn, int ntiles, int& m, int& n) {
 template <int FMT> struct BCodes;
 template <> struct BCodes<1> { u32x4_t c0, c1; u32x2_t sc; };
 template <> struct BCodes<2> { u32x2_t c0, c1; u32x2_t sc; };
+template <> struct BCodes<3> { u32x2_t c0, c1; u32x2_t sc; };  // q2 codes; sc.x = the two 64-block scales
 
 // Weight codes and activations are read through buffer resources: the
 // wave-uniform base and the chunk's offset live in scalar registers, the
@@ -494,7 +495,10 @@ __device__ __forceinline__ void load_bcodes(BCodes<FMT>& b, __amdgpu_buffer_rsrc
         b.c0 = __builtin_amdgcn_raw_buffer_load_b64(r, offc, soff, 0);
         b.c1 = __builtin_amdgcn_raw_buffer_load_b64(r, offc + 32 * 8, soff, 0);
     }
-    b.sc = __builtin_amdgcn_raw_buffer_load_b64(r, offs, soff, 0);
+    if constexpr (FMT == 3)
+        b.sc = u32x2_t{__builtin_amdgcn_raw_buffer_load_b32(r, offs, soff, 0), 0u};
+    else
+        b.sc = __builtin_amdgcn_raw_buffer_load_b64(r, offs, soff, 0);
 }
 
 __device__ __forceinline__ float ub0(uint32_t v) { return (float)(v & 0xFFu); }
@@ -536,14 +540,16 @@ __device__ __forceinline__ u32x4_t deq_q2(uint32_t w, float d, float c) {
 // converted exactly by v_fma_mix_f32; c costs one v_mul_f16 per block.
 // (Written with scalar halves: the same product over bit-cast f16x2 words
 // has been compiled to reuse the first word's products for the second.)
-__device__ __forceinline__ _Float16 scale_h(u32x2_t s, int j) {
+// (q2b64: block j of 32 weights takes the scale of 64-block j / 2, in sc.x.)
+template <int FMT> __device__ __forceinline__ _Float16 scale_h(u32x2_t s, int j) {
+    if constexpr (FMT == 3) return __builtin_bit_cast(_Float16, (uint16_t)((j & 2) ? (s.x >> 16) : (s.x & 0xFFFFu)));
     const uint32_t w = (j & 2) ? s.y : s.x;
     return __builtin_bit_cast(_Float16, (uint16_t)((j & 1) ? (w >> 16) : (w & 0xFFFFu)));
 }
 template <int FMT>
 __device__ __forceinline__ u32x4_t deq_half(const BCodes<FMT>& b, int ks, u32x2_t sc) {
     const int j = ks >> 1;
-    const _Float16 dh = scale_h(sc, j);
+    const _Float16 dh = scale_h<FMT>(sc, j);
     const _Float16 ch = dh * (_Float16)(FMT == 1 ? -8.f : -2.f);
     const float d = (float)dh, c = (float)ch;
     if constexpr (FMT == 1) {
@@ -764,7 +770,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // lane l takes the slot-lanes (n % 16, half) and (n % 16, half + 2) of its row tile
         const uint32_t tile = base + (uint32_t)min(rt, mg.rows / 16 - 1) * (uint32_t)mg.tile_bytes;
         it.boffc[gi] = tile + (uint32_t)((n & 15) + 16 * half) * QF<FMT>::kCW;
-        it.boffs[gi] = tile + 64 * QF<FMT>::kCW + (uint32_t)(n & 15) * 8;
+        it.boffs[gi] = tile + 64 * QF<FMT>::kCW + (uint32_t)(n & 15) * (FMT == 3 ? 4 : 8);
     }
     // A: lane l of instruction q of wave w fetches segment (l % 16) ^ (r % 16)
     // of tile row r = 32 w + 4 q + l / 16
@@ -894,12 +900,19 @@ static hipError_t launch_gemm(const uint16_t* x, const uint8_t* slots, const Geo
 hipError_t launch_pf_gemm1(const uint16_t* x, int T, const uint8_t* layer_slots, const Geom& g, PrefillBufs pb,
                            const Launch& lc) {
     pb.T = T;
-    return g.fmt == 1 ? launch_gemm<1, 1>(x, layer_slots, g, pb, lc) : launch_gemm<2, 1>(x, layer_slots, g, pb, lc);
+    switch (g.fmt) {
+        case 1: return launch_gemm<1, 1>(x, layer_slots, g, pb, lc);
+        case 2: return launch_gemm<2, 1>(x, layer_slots, g, pb, lc);
+        default: return launch_gemm<3, 1>(x, layer_slots, g, pb, lc);
+    }
 }
 
 hipError_t launch_pf_gemm2(const uint8_t* layer_slots, const Geom& g, PrefillBufs pb, const Launch& lc) {
-    return g.fmt == 1 ? launch_gemm<1, 2>(nullptr, layer_slots, g, pb, lc)
-                      : launch_gemm<2, 2>(nullptr, layer_slots, g, pb, lc);
+    switch (g.fmt) {
+        case 1: return launch_gemm<1, 2>(nullptr, layer_slots, g, pb, lc);
+        case 2: return launch_gemm<2, 2>(nullptr, layer_slots, g, pb, lc);
+        default: return launch_gemm<3, 2>(nullptr, layer_slots, g, pb, lc);
+    }
 }
 
 hipError_t launch_pf_combine(const uint16_t* x, int T, const Geom& g, PrefillBufs pb, uint16_t* y, int residual,

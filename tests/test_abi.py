@@ -37,7 +37,10 @@ def test_host_only_calls_without_gpu():
     assert moe.moe_expert_bytes(4096, 2048, moe.MOE_Q4B32) == 14_155_776
     assert moe.moe_expert_bytes(2560, 640, moe.MOE_Q2B32) == 1_536_000
     assert moe.moe_expert_bytes(100, 64, moe.MOE_Q4B32) == -1
-    assert moe.moe_expert_bytes(128, 64, 3) == -1
+    # q2b64: 2.25 bits per weight, hidden and ffn multiples of 64
+    assert moe.moe_expert_bytes(2560, 640, moe.MOE_Q2B64) == 1_382_400
+    assert moe.moe_expert_bytes(2560, 96, moe.MOE_Q2B64) == -1
+    assert moe.moe_expert_bytes(128, 64, 4) == -1
     lib = moe.lib()
     assert lib.moe_destroy(None) == moe.MOE_OK
     assert lib.moe_forward(None, None, None) == moe.MOE_EINVAL
