@@ -35,8 +35,9 @@
  *   MOE_Q2B64  BW 64, 18 bytes/block, weight j in byte j>>2 at bit 2*(j&3),     w = d*(q-2)
  * so one expert is 3*H*F/BW blocks (q4b32 at H=4096, F=2048: 14,155,776 bytes).
  * MOE_Q2B64 spends 2.25 bits per weight: 1,382,400 bytes per 2560 x 640
- * expert, the size of the 2-bit expert blob of the teardown page "Strata
- * 引擎深度拆解", section 二 (which does not print its layout; one fp16 scale
+ * expert, the size of the 2-bit expert blob on the page "Strata 改源码去跑
+ * DeepSeek V4 Flash？", section 三 item 4, and 34 GB for all experts of the
+ * Q2_0 tier in section 一 (the page does not print the layout; one fp16 scale
  * per 64 codes is the reading taken).
  *
  * Conventions for every call:

@@ -78,9 +78,10 @@ int64_t oracle_block_bytes(int fmt) {
 }
 
 /* Weights per block: 32, or 64 for q2b64 (one fp16 scale per 64 two-bit
- * codes, 2.25 bits per weight: the size of the 2-bit expert blob in the
- * teardown page "Strata 引擎深度拆解", section 二, 1,382,400 bytes per
- * 2560 x 640 expert, and of its 34 GB expert total). */
+ * codes, 2.25 bits per weight: the size of the 2-bit expert blob on the page
+ * "Strata 改源码去跑 DeepSeek V4 Flash？", section 三 item 4 (1,382,400 bytes
+ * per 2560 x 640 expert), and of the Q2_0 tier's 34 GB expert total, section
+ * 一 of the same page). */
 int oracle_block_weights(int fmt) { return fmt == ORACLE_Q2B64 ? 64 : 32; }
 
 /* Weight j (0..31, or 0..63 for q2b64) of one canonical block. */
