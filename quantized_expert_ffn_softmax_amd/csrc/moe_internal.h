@@ -106,7 +106,7 @@ struct RouteBufs {
 
 // Decode FFN scratch.
 struct DecodeBufs {
-    uint32_t* afrag;  // [maxA x nbF_pad x 64 x 4] v = w*SwiGLU as bf16 hi/lo MFMA A fragments
+    uint32_t* afrag;  // [maxA x nbF_pad x 64 x 4] v = w*SwiGLU as bf16 hi/lo MFMA A fragments (T <= 4: 32 lanes per block)
     float* spart;     // [maxA x nbF_pad x 2 x 16] per-half-block sums of the fragment rows
     float* part;      // [maxA x 8 x H] per-expert down projections
 };

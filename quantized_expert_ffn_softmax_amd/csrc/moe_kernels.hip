@@ -592,13 +592,16 @@ __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restric
     // v = w * silu(g) * u becomes the down projection's A operand, k = f, in
     // the layout of one MFMA fragment per 32-wide block of F: token t's bf16 hi
     // part in row 4 (t % 4) + 2 (t / 4) and its bf16 lo part in the row after,
-    // plus the per-half-block row sums of both parts.  All 16 rows are written
-    // (zeros for t >= T): with R = 1 lane group gs also writes the zero rows of
-    // token gs + 4.
+    // plus the per-half-block row sums of both parts (all 16 rows; zeros for
+    // t >= T).  R = 2: the fragment is stored whole (lane = row + 16 k-slice,
+    // 64 lanes).  R = 1 (T <= 4): rows 4 gs + 2, 4 gs + 3 are zero, and only
+    // the 32 lanes of rows 4t, 4t + 1 are stored, lane 8 k-slice + 2 t + (0 hi,
+    // 1 lo): half the fragment traffic and LDS of the down projection.
     const int nbFp = g.dn.nch * 4;
     const int bF = rt >> 1, kf = 16 * (rt & 1) + n;
-    uint16_t* af16 = reinterpret_cast<uint16_t*>(afrag) + ((int64_t)a * nbFp + bF) * 64 * 8 + 16 * (kf >> 3) * 8 +
-                     (kf & 7);
+    constexpr int FL = R == 1 ? 32 : 64;
+    uint16_t* af16 = reinterpret_cast<uint16_t*>(afrag) + ((int64_t)a * nbFp + bF) * FL * 8 + (kf & 7);
+    const int ksl = kf >> 3;  // k-slice of f inside the block
     float shi[R], slo[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -611,13 +614,9 @@ __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restric
         const uint32_t lo = f2bf(v - bf2f(hi));
         shi[i] = row_sum_f32(bf2f(hi));
         slo[i] = row_sum_f32(bf2f(lo));
-        const int rh = 4 * (t & 3) + 2 * (t >> 2);
-        af16[rh * 8] = (uint16_t)hi;
-        af16[(rh + 1) * 8] = (uint16_t)lo;
-    }
-    if constexpr (R == 1) {  // token gs + 4: rows 4 gs + 2, 4 gs + 3
-        af16[(4 * gs + 2) * 8] = 0;
-        af16[(4 * gs + 3) * 8] = 0;
+        const int fl = R == 1 ? 8 * ksl + 2 * t : 4 * (t & 3) + 2 * (t >> 2) + 16 * ksl;
+        af16[fl * 8] = (uint16_t)hi;
+        af16[(fl + 1) * 8] = (uint16_t)lo;
     }
     if (n == 0) {
         float* sp = spart + (((int64_t)a * nbFp + bF) * 2 + (rt & 1)) * 16;
@@ -692,7 +691,8 @@ constexpr int kRing = 8;  // chunks in flight per wave beyond the one being mult
 // (wave w: row tile 8rg+w).  The workgroup first requests the expert's A
 // fragments (token t: v hi in row 4 (t % 4) + 2 (t / 4), v lo in the row
 // after, so a lane's result registers 0, 1 hold token lane / 16 and 2, 3 token
-// lane / 16 + 4; NV = 2 for T <= 4 skips the latter), then each wave requests the
+// lane / 16 + 4; NV = 2 for T <= 4 skips the latter and stages the compact
+// 32-lane fragments: the lanes of the zero rows take a zero operand), then each wave requests the
 // first kRing chunks of its row tile; the fragments go to LDS as soon as they
 // arrive and every further chunk is requested as one is consumed.  K = F fits
 // one pass (nch <= NC).  Output: part[a][t][row].
@@ -715,9 +715,14 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots
     const bool live = rt < g.H / 16;
     const uint8_t* Dt = slots + (int64_t)e * g.slot_bytes + g.d_off + (int64_t)(live ? rt : 0) * md.tile_bytes;
     constexpr int CWN = FMT == 1 ? 4 : 2;
+    constexpr int FL = NV == 2 ? 32 : 64;  // fragment lanes stored per block
+    // this lane's fragment entry; the lanes of zero rows (compact form) read
+    // their neighbour's (the same address: a broadcast) and use zero
+    const int fl = NV == 2 ? 8 * (lane >> 4) + 2 * ((lane & 15) >> 2) + (lane & 1) : lane;
+    const bool fzero = NV == 2 && (lane & 2);
     u32x4_t* frag = reinterpret_cast<u32x4_t*>(smem);
     StageRegs<FPER> fst;
-    fst.issue(reinterpret_cast<const u32x4_t*>(afrag) + (int64_t)a * nbp * 64, nbp * 64);
+    fst.issue(reinterpret_cast<const u32x4_t*>(afrag) + (int64_t)a * nbp * FL, nbp * FL);
     const float* sp = spart + (int64_t)a * nbp * 32;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, corr = acc;
     // ring depth: kRing chunks, 4 for the 16-chunk case (register budget)
@@ -736,13 +741,17 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots
         load_codes<FMT>(Dt + off, lane, cw[i]);
         sc[i] = load_scales<FMT>(Dt + off, n);
     };
-    // The fragments of all 8 token rows (zeros for t >= T) and of the padded
-    // blocks (zeros, never written) are defined, so nothing is masked; chunks
+    // The fragments of all token rows are written (zeros for t >= T); chunks
     // past nch (NC > nch) carry zero scales and add nothing.
     auto compute = [&](int c, int i) {
         u32x4_t A[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) A[j] = frag[min(c * 4 + j, nbp - 1) * 64 + lane];
+        for (int j = 0; j < 4; ++j) {
+            // padding blocks (K past F) take a zero operand too: their staged
+            // entries may hold fragments of a call with the other layout
+            const u32x4_t f = frag[min(c * 4 + j, nbp - 1) * FL + fl];
+            A[j] = fzero || c * 4 + j >= md.nb ? u32x4_t{0u, 0u, 0u, 0u} : f;
+        }
         const u32x2_t scc = c < md.nch ? sc[i] : u32x2_t{0u, 0u};  // padding chunk (NC > nch): zero scales
         chunk_mac<FMT, NV>(cw[i], scc, A, s0[i] + s1[i], gs, acc, corr);
     };
@@ -751,7 +760,7 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots
         load(i, i);
         __builtin_amdgcn_sched_barrier(0);  // chunk order kept: the math on chunk i waits for chunk i only
     }
-    fst.commit(frag, nbp * 64, [](int q) { return q; }, nbp * 64);
+    fst.commit(frag, nbp * FL, [](int q) { return q; }, nbp * FL);
     __syncthreads();
     // waves past the last row tile compute on tile 0 and discard the result:
     // no branch around the refill loads
@@ -801,7 +810,7 @@ hipError_t launch_down_f(int T, const uint8_t* slots, const Geom& g, RouteBufs r
 template <int FMT, int NC>
 hipError_t launch_down_nc(int T, const uint8_t* slots, const Geom& g, RouteBufs rb, DecodeBufs db, dim3 grid, int lds,
                           int maxA, const Launch& lc) {
-    const int per = (g.dn.nch * 4 * 64 + 511) / 512;  // <= 8 (F <= 2048)
+    const int per = (g.dn.nch * 4 * (T <= 4 ? 32 : 64) + 511) / 512;  // <= 8 (F <= 2048)
     if (per <= 2) return launch_down_f<FMT, NC, 2>(T, slots, g, rb, db, grid, lds, maxA, lc);
     if (per <= 4) return launch_down_f<FMT, NC, 4>(T, slots, g, rb, db, grid, lds, maxA, lc);
     return launch_down_f<FMT, NC, 8>(T, slots, g, rb, db, grid, lds, maxA, lc);
@@ -810,7 +819,7 @@ hipError_t launch_down_nc(int T, const uint8_t* slots, const Geom& g, RouteBufs 
 hipError_t launch_down_decode(int T, const uint8_t* layer_slots, const Geom& g, RouteBufs rb, DecodeBufs db, int maxA,
                               const Launch& lc) {
     const int maxA_T = (g.E < T * g.k ? g.E : T * g.k) + g.S;
-    const int lds = g.dn.nch * 4 * 64 * 16 + 16;  // + the dummy slot of the staging stores
+    const int lds = g.dn.nch * 4 * (T <= 4 ? 32 : 64) * 16 + 16;  // fragments + the dummy slot of the staging stores
     dim3 grid((g.H + kDownRowsPerWG - 1) / kDownRowsPerWG, maxA_T);
     const int nch = g.dn.nch;  // <= 16 (F <= 2048)
 #define MOE_DOWN_CASE(F, N) \
