@@ -481,9 +481,10 @@ hipError_t launch_topk_sort_decode(int T, const Geom& g, RouteBufs rb, const int
 // compiler counts them) right after the workgroup's share of x, which is
 // written to LDS as soon as it arrives, with the weights still in flight.
 // The MFMA computes C[m][n = row] with A = x: row m = 4 g + i carries token
-// R g + i for i < R (R = 1 for T <= 4, else 2) and reads the zero row
-// otherwise, so a lane's results for its tokens sit in its first R result
-// registers and only those are scaled.
+// R g + i for i < R (R = 1 for T <= 4, else 2), so a lane's results for its
+// tokens sit in its first R result registers and only those are scaled and
+// used; the other rows read some token's row and their results are ignored
+// (the MFMA rows are independent), so LDS holds just the T rows of x.
 // Output: v = w_t,a * silu(g) * u as the bf16 hi/lo A fragments of the down
 // projection, and their per-half-block sums.
 // (slots and sx are deliberately not __restrict__: with it the compiler may
@@ -513,6 +514,11 @@ __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restric
     const uint8_t* Gt = slots + base + g.g_off;
     const uint8_t* Ut = slots + base + g.u_off;
     const int h8 = g.H / 8, xs8 = h8 + 1;
+    // [T][H + 8]: rows padded against bank conflicts
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+    const float inv_h8 = 1.0f / (float)h8;  // q < 4096, h8 <= 512: (q + 0.5) / h8 is never within 1e-3 of an integer
+    // element q of row t lands at q + t (rows are h8 + 1 elements apart in LDS)
+    const auto xslot = [=](int q) { return q + (int)(((float)q + 0.5f) * inv_h8); };
     StageRegs<XPER> xst;
     xst.issue(reinterpret_cast<const u32x4_t*>(x), T * h8);
     uint32_t cg[NC][CWN], cu[NC][CWN];
@@ -538,23 +544,9 @@ __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restric
 #pragma unroll
     for (int i = 0; i < R; ++i) wt[i] = wtab[a * kMaxDecodeT + R * gs + i];
     const int xstride = g.H + 8;
-    // [T + 1][H + 8]: rows padded against bank conflicts; row T is zero and is
-    // what the MFMA rows m >= T read, so the A operands need no masking
-    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {  // xs8 <= 513 elements of 16 bytes
-        const int i = threadIdx.x + 256 * j;
-        if (i < xs8) reinterpret_cast<u32x4_t*>(xs)[T * xs8 + i] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-    {
-        const float inv_h8 = 1.0f / (float)h8;  // q < 4096, h8 <= 512: (q + 0.5) / h8 is never within 1e-3 of an integer
-        // element q of row t lands at q + t (rows are h8 + 1 elements apart in LDS)
-        xst.commit(reinterpret_cast<u32x4_t*>(xs), T * h8, [=](int q) {
-            return q + (int)(((float)q + 0.5f) * inv_h8);
-        }, (T + 1) * xs8);
-    }
+    xst.commit(reinterpret_cast<u32x4_t*>(xs), T * h8, xslot, T * xs8);
     __syncthreads();
-    const uint16_t* xl = xs + (mt < T ? mt : T) * xstride + 8 * gs;
+    const uint16_t* xl = xs + (mt < T ? mt : 0) * xstride + 8 * gs;
     f32x4_t accG = {0.f, 0.f, 0.f, 0.f}, accU = accG, corG = accG, corU = accG;
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
@@ -637,12 +629,12 @@ template <int FMT, int NC, int XPER, int R>
 hipError_t launch_gateup_r(const uint16_t* x, int T, const uint8_t* slots, const Geom& g, RouteBufs rb,
                            DecodeBufs db, int maxA_T, int maxA, const Launch& lc) {
     static int granted = 64 * 1024;
-    const int xbytes = (T + 1) * (g.H + 8) * 2 + 16;  // + the zero row and the dummy slot of the staging stores
+    const int xbytes = T * (g.H + 8) * 2 + 16;  // + the dummy slot of the staging stores
     const int lds = xbytes > 3 * 4 * 64 * 16 ? xbytes : 3 * 4 * 64 * 16;
     hipError_t e = ensure_lds(k_gateup_decode<FMT, NC, XPER, R>, lds, granted);
     if (e != hipSuccess) return e;
-    launch(k_gateup_decode<FMT, NC, XPER, R>, dim3(maxA_T * (g.F / 16)), dim3(256), lds, lc, x, T, slots, g, rb.sx,
-           rb.nact, rb.act, rb.wtab, maxA, db.afrag, db.spart);
+    launch(k_gateup_decode<FMT, NC, XPER, R>, dim3(maxA_T * (g.F / 16)), dim3(256), lds, lc, x, T, slots, g,
+           rb.sx, rb.nact, rb.act, rb.wtab, maxA, db.afrag, db.spart);
     return hipGetLastError();
 }
 
@@ -725,8 +717,10 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots
     fst.issue(reinterpret_cast<const u32x4_t*>(afrag) + (int64_t)a * nbp * FL, nbp * FL);
     const float* sp = spart + (int64_t)a * nbp * 32;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, corr = acc;
-    // ring depth: kRing chunks, 4 for the 16-chunk case (register budget)
-    constexpr int R = NC < kRing ? NC : (NC > 8 ? 4 : kRing);
+    // ring depth: kRing chunks; 2 for the 16-chunk case, which keeps the kernel
+    // at 58 VGPRs (8 waves per SIMD: every workgroup of a 43-layer-chain-sized
+    // call resident at once, measured faster than a deeper ring)
+    constexpr int R = NC < kRing ? NC : (NC > 8 ? 2 : kRing);
     uint32_t cw[R][CWN];
     u32x2_t sc[R];
     float s0[R], s1[R];
