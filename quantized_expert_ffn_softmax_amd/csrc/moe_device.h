@@ -88,12 +88,14 @@ template <> __device__ __forceinline__ u32x4_t unpack<3>(const uint32_t* cw, int
     return unpack<2>(cw, j, k);
 }
 
+// Expert weights are read once per call: non-temporal loads keep them from
+// displacing the activations and operand fragments in the caches.
 template <int FMT> __device__ __forceinline__ void load_codes(const uint8_t* chunk, int lane, uint32_t* cw) {
     if constexpr (FMT == 1) {
-        u32x4_t v = *reinterpret_cast<const u32x4_t*>(chunk + lane * 16);
+        u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(chunk + lane * 16));
         cw[0] = v.x; cw[1] = v.y; cw[2] = v.z; cw[3] = v.w;
     } else {
-        u32x2_t v = *reinterpret_cast<const u32x2_t*>(chunk + lane * 8);
+        u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(chunk + lane * 8));
         cw[0] = v.x; cw[1] = v.y;
     }
 }
@@ -101,9 +103,10 @@ template <int FMT> __device__ __forceinline__ void load_codes(const uint8_t* chu
 // (block j of 32 weights takes the scale of 64-block j / 2).
 template <int FMT> __device__ __forceinline__ u32x2_t load_scales(const uint8_t* chunk, int n) {
     if constexpr (FMT == 3)
-        return u32x2_t{*reinterpret_cast<const uint32_t*>(chunk + 64 * QF<FMT>::kCW + n * 4), 0u};
+        return u32x2_t{__builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(chunk + 64 * QF<FMT>::kCW + n * 4)),
+                       0u};
     else
-        return *reinterpret_cast<const u32x2_t*>(chunk + 64 * QF<FMT>::kCW + n * 8);
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(chunk + 64 * QF<FMT>::kCW + n * 8));
 }
 template <int FMT> __device__ __forceinline__ float scale_of(u32x2_t s, int j) {
     if constexpr (FMT == 3) return h2f((j & 2) ? (s.x >> 16) : (s.x & 0xFFFFu));
