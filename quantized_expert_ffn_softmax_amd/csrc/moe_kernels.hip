@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restric
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int seg = min(lane + 64 * j, ns - 1);
-        wv[j] = *reinterpret_cast<const u32x4_t*>(Wr + (int64_t)e * H + h0 + 8 * seg);
+        wv[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Wr + (int64_t)e * H + h0 + 8 * seg));
 #pragma unroll
         for (int t = 0; t < TT; ++t)
             xv[j][t] = *reinterpret_cast<const u32x4_t*>(x + (int64_t)min(t, T - 1) * H + h0 + 8 * seg);
