@@ -206,3 +206,18 @@ def test_create_rejects_bad_geometry(torch_cuda):
         with pytest.raises(MoEError) as ei:
             MoEContext(4096, 2048, 1024, 1, 8, 64, Q4, 4)  # 64 x 1025 experts x 14.2 MB
         assert ei.value.status == MOE_ENOMEM
+
+
+# The decode limits at once: 1024 experts (16 logits per lane), top-16, a
+# shared expert, an 8-token window (128 pairs, up to 129 active experts),
+# hidden 4096 (two 16-byte segments per lane in the router).
+MAX_DECODE = MoEConfig("max_decode", (8,), 4096, 64, 1024, 1, 16, 1, Q2B32, mi.BIAS_ZIPF, 0.3)
+
+
+@pytest.mark.parametrize("T", [1, 4, 8])
+def test_decode_at_the_size_limits(torch_cuda, T):
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    cfg = MAX_DECODE
+    with MoEContext.from_config(cfg) as ctx:
+        W, b, ex = load_layer(ctx, cfg, 12, 0)
+        _check_layer(ctx, cfg, 12, 0, T, T, W, b, ex, f"max_decode/T{T}")

@@ -198,3 +198,13 @@ def test_decode_and_prefill_agree_on_routing(torch_cuda):
         ids16, w16, _, _ = ctx.route(0, to_dev_bf16(x))
         np.testing.assert_array_equal(ids8.cpu().numpy(), ids16.cpu().numpy()[:8])
         assert np.abs(w8.cpu().numpy() - w16.cpu().numpy()[:8]).max() <= 1e-7
+
+
+def test_long_chunk_many_sort_blocks(torch_cuda):
+    """A 12,000-token chunk: 47 256-token sort blocks, several 128-row M-blocks
+    per expert, a shared expert over every token."""
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    cfg = MoEConfig("pf_long", (12000,), 256, 128, 64, 1, 8, 1, Q4B32, mi.BIAS_ZIPF, 0.5)
+    with MoEContext.from_config(cfg, max_tokens=12000) as ctx:
+        W, b, ex = load_layer(ctx, cfg, 13, 0)
+        _check_full(ctx, cfg, 13, 0, 0, 12000, W, b, ex, "long/T12000")
