@@ -875,9 +875,11 @@ hipError_t launch_rmsnorm(const uint16_t* x, int T, int H, uint16_t* h, const La
 // ---------------------------------------------------------------- combine
 // y[t][h] = bf16( sum_{a < nact} part[a][t][h]  (+ x[t][h]) ), experts added in
 // ascending active order (routed experts by id, then the shared expert).  The
-// partials are requested 16 at a time (unconditional loads, clamped index;
-// entries past nact are added as zeros), so the sum costs ceil(nact / 16)
-// memory round trips.
+// partials are requested 32 at a time (unconditional loads, clamped index;
+// entries past nact are added as zeros), so the sum costs ceil(nact / 32)
+// memory round trips (one for the decode shapes' 20-30 active experts); the
+// residual is requested with the first batch.
+constexpr int kCombineBatch = 32;
 __global__ __launch_bounds__(256) void k_combine_decode(const uint16_t* __restrict__ x, int T, int H,
                                                         const int32_t* __restrict__ nact,
                                                         const float* __restrict__ part, uint16_t* __restrict__ y,
@@ -885,17 +887,18 @@ __global__ __launch_bounds__(256) void k_combine_decode(const uint16_t* __restri
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= T * H) return;
     const int nA = nact[0];
+    const float xr = bf2f(x[i]);
     const float* p = part + i;  // part[a][t][h] with t*H + h = i
     const int64_t stride = (int64_t)kMaxDecodeT * H;
     float s = 0.f;
-    for (int a0 = 0; a0 < nA; a0 += 16) {
-        float v[16];
+    for (int a0 = 0; a0 < nA; a0 += kCombineBatch) {
+        float v[kCombineBatch];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) v[q] = p[min(a0 + q, nA - 1) * stride];
+        for (int q = 0; q < kCombineBatch; ++q) v[q] = p[min(a0 + q, nA - 1) * stride];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) s += a0 + q < nA ? v[q] : 0.f;
+        for (int q = 0; q < kCombineBatch; ++q) s += a0 + q < nA ? v[q] : 0.f;
     }
-    if (residual) s += bf2f(x[i]);
+    if (residual) s += xr;
     y[i] = (uint16_t)f2bf(s);
 }
 
