@@ -200,6 +200,18 @@ template <int CTRL, int ROWS> __device__ __forceinline__ void max_bcast_u32(uint
     const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)k, (int)k, CTRL, ROWS, 0xF, false);
     k = o > k ? o : k;
 }
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each
+// row of 16 (lanes shifted in from outside the row add 0), then row 15's total
+// into rows 1 and 3 and row 31's into rows 2 and 3 (DPP row broadcasts).
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return v;
+}
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t k) {
     max_step_u32<kDppXor1>(k);
     max_step_u32<kDppXor2>(k);

@@ -416,11 +416,7 @@ __global__ __launch_bounds__(256) void k_topk_sort(int T, int E, int k, int S, R
         p[j] = ((uint32_t)__popc(mk) << 16) | (mk ? 1u : 0u);
         tot += p[j];
     }
-    uint32_t incl = tot;
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
+    const uint32_t incl = wave_incl_scan_u32(tot);
     if (lane == 63) s_wsum[wave] = incl;
     __syncthreads();
     uint32_t ex = incl - tot;
