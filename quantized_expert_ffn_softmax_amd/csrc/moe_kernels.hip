@@ -3,7 +3,8 @@
 // Per layer and call (T <= 8 tokens), five launches:
 //   k_router_decode   one workgroup per expert: router GEMV (+bias) with fp64
 //                     accumulation of the exact bf16 x bf16 products; also
-//                     the per-block sums of x
+//                     the per-block sums of x (and, for chain layers, the
+//                     per-token RMS pre-norm of x)
 //   k_topk_sort       one workgroup: top-k per token (logit descending, lower
 //                     id on ties; DPP wave maxima over pre-sorted per-lane
 //                     lists of 32-bit keys), renormalised softmax
@@ -12,9 +13,9 @@
 //                     and weight table
 //   k_gateup_decode   one workgroup per (active expert, 16-row tile of F):
 //                     fused dequant + gate/up GEMV on bf16 MFMA + SwiGLU; all
-//                     weight loads issued on entry, whole grid resident at
-//                     once; writes v = w * SwiGLU as bf16 hi/lo halves in
-//                     MFMA-operand order
+//                     weight loads issued on entry (non-temporal); writes
+//                     v = w * SwiGLU as bf16 hi/lo halves in MFMA-operand
+//                     order
 //   k_down_decode     per (active expert, 128-row group of H): down GEMV with
 //                     the expert's operand staged once in LDS; stores one
 //                     partial row block per expert
@@ -713,9 +714,9 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots
     fst.issue(reinterpret_cast<const u32x4_t*>(afrag) + (int64_t)a * nbp * FL, nbp * FL);
     const float* sp = spart + (int64_t)a * nbp * 32;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, corr = acc;
-    // ring depth: kRing chunks; 2 for the 16-chunk case, which keeps the kernel
-    // at 58 VGPRs (8 waves per SIMD: every workgroup of a 43-layer-chain-sized
-    // call resident at once, measured faster than a deeper ring)
+    // ring depth: kRing chunks; 2 for the 16-chunk case (F = 2048), which keeps
+    // the kernel at 58 VGPRs, i.e. 8 waves per SIMD, so that a DeepSeek-shaped
+    // call's whole grid is resident at once (measured faster than a ring of 4)
     constexpr int R = NC < kRing ? NC : (NC > 8 ? 2 : kRing);
     uint32_t cw[R][CWN];
     u32x2_t sc[R];
