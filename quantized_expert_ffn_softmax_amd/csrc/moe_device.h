@@ -300,25 +300,4 @@ template <int PER> struct StageRegs {
     }
 };
 
-// Copy n16 16-byte elements from global memory to LDS with the whole
-// workgroup; every thread issues up to 8 loads before its first LDS store, so
-// the copy costs one memory latency.  dst_index maps a source element index
-// to its LDS element index (row padding).
-template <class Map>
-__device__ __forceinline__ void stage_lds(u32x4_t* dst, const u32x4_t* __restrict__ src, int n16, Map dst_index) {
-    for (int i0 = threadIdx.x; i0 < n16; i0 += blockDim.x * 8) {
-        u32x4_t v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = i0 + j * (int)blockDim.x;
-            if (i < n16) v[j] = src[i];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = i0 + j * (int)blockDim.x;
-            if (i < n16) dst[dst_index(i)] = v[j];
-        }
-    }
-}
-
 }  // namespace moe
