@@ -206,7 +206,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
         const size_t P = (size_t)Tm * g.k, rows = P + (size_t)g.S * Tm;
         const size_t nblk = (size_t)(Tm + kPfBlockTokens - 1) / kPfBlockTokens;
         c->pb.max_tiles = prefill_max_tiles(Tm, g.k, g.E, g.S);
-        p_logits = cv.take<float>((size_t)Tm * g.E);
+        p_logits = cv.take<float>((size_t)pf_router_partial_floats(Tm, g.E));
         p_ids = cv.take<int32_t>(P);
         p_w = cv.take<float>(P);
         p_blkcnt = cv.take<uint32_t>(nblk * g.E);

@@ -117,7 +117,7 @@ constexpr int kDownRowsPerWG = 128;  // 8 waves x 16 rows
 constexpr int kPfBlockTokens = 256;  // tokens per counting-sort block
 constexpr int kPfTileRows = 128;     // rows of one grouped-GEMM M-block
 struct PrefillBufs {
-    float* logits;     // [T x E]   fp32 MFMA logits (+ bias)
+    float* logits;     // [ksplit x T x E] fp32 MFMA partial logits (K split; no bias)
     int32_t* ids;      // [T x k]
     float* w;          // [T x k]
     uint32_t* blkcnt;  // [nblk x E] pairs per (token block, expert)
@@ -133,7 +133,23 @@ struct PrefillBufs {
     float* o;          // [(T*k + S*T) x H] fp32 per-row expert outputs
     int max_tiles;
     int T;             // tokens of the current call (set by the GEMM launchers on their copy)
+    int ksplit;        // K split of the router logits (set by the top-k launcher on its copy)
 };
+// K split of the prefill router GEMM: doubled (up to 8, keeping H / 32 a
+// multiple) while the 128 x 256 tiles times the split fill at most 256
+// workgroups, so a chunk of a few thousand tokens still covers the CUs.
+inline int pf_router_splits(int T, int E, int H) {
+    const int tiles = ((T + 127) / 128) * ((E + 255) / 256);
+    int ks = 1;
+    while (ks < 8 && tiles * ks * 2 <= 256 && (H / 32) % (ks * 2) == 0) ks *= 2;
+    return ks;
+}
+// floats of the partial-logit buffer for chunks of up to Tm tokens: with a
+// split, the tiles times the split are at most 256 (so ks T E <= 256 x 128 x 256)
+inline int64_t pf_router_partial_floats(int Tm, int E) {
+    const int64_t one = (int64_t)Tm * E;
+    return std::max<int64_t>(one, std::min<int64_t>(8 * one, 256LL * 128 * 256));
+}
 inline int prefill_max_tiles(int T, int k, int E, int S) {
     const int64_t P = (int64_t)T * k;
     return (int)((P + kPfTileRows - 1) / kPfTileRows + std::min<int64_t>(E, P) +

@@ -8,7 +8,9 @@
 // ("Strata 改源码去跑 DeepSeek V4 Flash？", section 二: routed top-k experts
 // plus an always-on shared expert).
 //
-//   k_pf_router   logits = x Wr^T + b on v_mfma_f32_32x32x16_bf16 (fp32)
+//   k_pf_router   x Wr^T on v_mfma_f32_32x32x16_bf16 (fp32), 128 x 256 tiles
+//                 staged in LDS by DMA, K split into up to 8 partial sums
+//                 (added in order, with the bias, by the top-k kernel)
 //   k_pf_topk     one wave per token: candidates = every expert whose fp32
 //                 logit lies within twice the fp32 error bound of the k-th
 //                 largest; candidates re-scored exactly (fp64 sum of the exact
@@ -79,42 +81,116 @@ __global__ __launch_bounds__(256) void k_router_stats(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------- router (MFMA, fp32)
-// Grid (ceil(E/64), ceil(T/64)), 256 threads: wave (wm, wn) computes a 32x32
-// tile of logits, A = x rows (tokens), B = router rows (experts), straight
-// from global memory (rows clamped, results masked).  Lane l holds row l%32,
-// k = 8(l/32)..+7 of each 16-wide K step.
+// Grid (ceil(E/256), ceil(T/128), KS), 256 threads: workgroup (n, m, s)
+// computes the 128 x 256 tile (tokens 128 m.., experts 256 n..) of the
+// partial sums over K = [s H/KS, (s+1) H/KS) and stores them unrounded to
+// part[s][t][e]; the top-k kernel adds the KS partials in order and the bias.
+// Wave (wm, wn) owns rows 64 wm.. and columns 128 wn.. (2 x 4 MFMA tiles of
+// 32 x 32).  K advances in chunks of 32: the A tile (128 rows of x) and the B
+// tile (256 router rows) of a chunk, 4 16-byte segments per row, are copied to
+// LDS by buffer-load DMA (each instruction fills 64 consecutive slots), three
+// chunks ahead; segment p of row r sits in slot 4 r + (p ^ ((r / 4) % 4)), so
+// the MFMA operand reads (32 rows, one segment) hit 32 distinct banks groups.
+// A wave issues exactly 6 DMA instructions per chunk and no other vector
+// loads in the loop, so "at most 6 c loads outstanding" means every chunk
+// older than the c newest has landed.
+constexpr int kPrRows = 128, kPrCols = 256, kPrBuf = 4;
+constexpr int kPrBufBytes = (kPrRows + kPrCols) * 4 * 16;  // 24 KB per chunk
+constexpr int kPrLds = kPrBuf * kPrBufBytes;
+
+__device__ __forceinline__ void pr_wait(int chunks_after) {
+    // s_waitcnt vmcnt(6 c): immediates for c = 0..2
+    if (chunks_after >= 2) __builtin_amdgcn_s_waitcnt(0x0F7C);       // vmcnt(12)
+    else if (chunks_after == 1) __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                         // vmcnt(0)
+}
+
 __global__ __launch_bounds__(256) void k_pf_router(const uint16_t* __restrict__ x, int T,
-                                                   const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
-                                                   int E, int H, float* __restrict__ logits) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.y * 64 + (wave >> 1) * 32, e0 = blockIdx.x * 64 + (wave & 1) * 32;
-    const int tr = min(t0 + (lane & 31), T - 1), er = min(e0 + (lane & 31), E - 1);
-    const uint16_t* xa = x + (int64_t)tr * H + 8 * (lane >> 5);
-    const uint16_t* wb = Wr + (int64_t)er * H + 8 * (lane >> 5);
-    f32x16_t acc;
+                                                   const uint16_t* __restrict__ Wr, int E, int H, int klen,
+                                                   float* __restrict__ part) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int e0 = blockIdx.x * kPrCols, t0 = blockIdx.y * kPrRows, ks = blockIdx.z;
+    const int nk = klen / 32;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, T * H * 2,
+                                                                        0x00020000);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Wr), 0, E * H * 2,
+                                                                        0x00020000);
+    // this wave's 6 instructions per chunk: q = wave + 4 j; q < 8 fills A slots
+    // 64 q.., else B slots 64 (q - 8)..; the lane's source segment (byte offset
+    // in x or Wr; the chunk adds its K offset as the scalar offset)
+    uint32_t voff[6];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    int k0 = 0;
-    for (; k0 + 64 <= H; k0 += 64) {
-        u32x4_t a[4], b[4];
+    for (int j = 0; j < 6; ++j) {
+        const int q = wave + 4 * j;
+        const int slot = 64 * (q < 8 ? q : q - 8) + lane;
+        const int r = slot >> 2, p = (slot & 3) ^ ((r >> 2) & 3);
+        const int row = q < 8 ? min(t0 + r, T - 1) : min(e0 + r, E - 1);
+        voff[j] = (uint32_t)((row * H + 8 * p) * 2);
+    }
+    auto issue = [&](int kc) {
+        uint8_t* buf = smem + (kc % kPrBuf) * kPrBufBytes;
+        const uint32_t soff = (uint32_t)((ks * klen + kc * 32) * 2);
+#pragma unroll
+        for (int j = 0; j < 6; ++j) {
+            const int q = wave + 4 * j;
+            uint8_t* dst = buf + (q < 8 ? 0 : kPrRows * 64) + 1024 * (q < 8 ? q : q - 8);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 8 ? xr : wr, (__attribute__((address_space(3))) void*)dst,
+                                                     16, voff[j], soff, 0, 0);
+        }
+    };
+    const int wm = wave & 1, wn = wave >> 1;
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    for (int c = 0; c < kPrBuf - 1 && c < nk; ++c) issue(c);
+    for (int kc = 0; kc < nk; ++kc) {
+        // this wave's DMA of chunk kc has landed; the barrier makes it so for
+        // every wave (a bare barrier: a release fence would wait for the DMA
+        // of the newer chunks too), and the acquire keeps the LDS reads after it
+        pr_wait(min(kPrBuf - 2, nk - 1 - kc));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        // the buffer of chunk kc - 1 is free: every wave has passed this barrier
+        if (kc + kPrBuf - 1 < nk) issue(kc + kPrBuf - 1);
+        const u32x4_t* sa = reinterpret_cast<const u32x4_t*>(smem + (kc % kPrBuf) * kPrBufBytes);
+        const u32x4_t* sb = sa + kPrRows * 4;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int p = 2 * st + (lane >> 5);
+            u32x4_t a[2], b[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = 64 * wm + 32 * i + (lane & 31);
+                a[i] = sa[4 * r + (p ^ ((r >> 2) & 3))];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 128 * wn + 32 * j + (lane & 31);
+                b[j] = sb[4 * r + (p ^ ((r >> 2) & 3))];
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+        }
+    }
+    // lane holds C[m = 8(v/4) + 4(lane/32) + v%4][n = lane%32] of each tile
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            a[j] = *reinterpret_cast<const u32x4_t*>(xa + k0 + 16 * j);
-            b[j] = *reinterpret_cast<const u32x4_t*>(wb + k0 + 16 * j);
+            const int e = e0 + 128 * wn + 32 * j + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int t = t0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (t < T && e < E) part[((int64_t)ks * T + t) * E + e] = acc[i][j][v];
+            }
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc = mfma32(a[j], b[j], acc);
-    }
-    for (; k0 < H; k0 += 16)
-        acc = mfma32(*reinterpret_cast<const u32x4_t*>(xa + k0), *reinterpret_cast<const u32x4_t*>(wb + k0), acc);
-    // lane holds C[m = 8(i/4) + 4(lane/32) + i%4][n = lane%32]
-    const int e = e0 + (lane & 31);
-    const float be = (bias && e < E) ? bias[e] : 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int t = t0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (t < T && e < E) logits[(int64_t)t * E + e] = acc[i] + be;
-    }
 }
 
 // ---------------------------------------------------------------- top-k (exact)
@@ -194,7 +270,11 @@ __global__ __launch_bounds__(256) void k_pf_topk(const uint16_t* __restrict__ x,
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int e = lane + 64 * j;
-        lf[j] = pb.logits[(int64_t)t * E + min(e, E - 1)];
+        // fp32 logit: the router's K-split partials added in order, then the bias
+        const int ec = min(e, E - 1);
+        float sl = pb.logits[(int64_t)t * E + ec];
+        for (int q = 1; q < pb.ksplit; ++q) sl += pb.logits[((int64_t)q * T + t) * E + ec];
+        lf[j] = sl + (bias ? bias[ec] : 0.f);
         key[j] = order_key((double)lf[j]);
         if (e >= E) taken |= 1u << j;
     }
@@ -844,12 +924,19 @@ hipError_t launch_router_stats(const uint16_t* Wr, const float* bias, int E, int
 
 hipError_t launch_pf_router(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const Geom& g,
                             PrefillBufs pb, const Launch& lc) {
-    launch(k_pf_router, dim3((g.E + 63) / 64, (T + 63) / 64), dim3(256), 0, lc, x, T, Wr, bias, g.E, g.H, pb.logits);
+    (void)bias;  // added by the top-k kernel
+    static int granted = 64 * 1024;
+    hipError_t e = ensure_lds(k_pf_router, kPrLds, granted);
+    if (e != hipSuccess) return e;
+    const int ks = pf_router_splits(T, g.E, g.H);
+    launch(k_pf_router, dim3((g.E + kPrCols - 1) / kPrCols, (T + kPrRows - 1) / kPrRows, ks), dim3(256), kPrLds, lc,
+           x, T, Wr, g.E, g.H, g.H / ks, pb.logits);
     return hipGetLastError();
 }
 
 hipError_t launch_pf_topk(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const float* rstat,
                           const Geom& g, PrefillBufs pb, int32_t* trace_ids, float* trace_w, const Launch& lc) {
+    pb.ksplit = pf_router_splits(T, g.E, g.H);
     const dim3 grid((T + 3) / 4);
     if (g.E <= 64)
         launch(k_pf_topk<1>, grid, dim3(256), 0, lc, x, T, Wr, bias, rstat, g.E, g.H, g.k, pb, trace_ids, trace_w);
