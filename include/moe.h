@@ -215,7 +215,8 @@ typedef enum {
     MOE_K_PF_GEMM1 = 8,     /* prefill grouped GEMM gate/up + SwiGLU */
     MOE_K_PF_GEMM2 = 9,     /* prefill grouped GEMM down */
     MOE_K_PF_COMBINE = 10,  /* prefill weighted combine */
-    MOE_K_NORM = 11         /* per-token RMS pre-norm (MOE_FWD_PRENORM) */
+    MOE_K_NORM = 11         /* per-token RMS pre-norm (MOE_FWD_PRENORM; prefill only: decode windows normalise
+                               inside the router kernel) */
 } moe_kernel_kind;
 
 typedef struct {
@@ -230,7 +231,8 @@ typedef struct {
  * forgets all recorded launches.  Profiling keeps at most 65536 launches. */
 moe_status moe_profile_read(moe_ctx* ctx, moe_kernel_time* out, int32_t cap, int32_t* n_out);
 
-/* Canonical bytes of one expert (3*H*F/32 blocks), or -1 for a bad shape. */
+/* Canonical bytes of one expert (3*H*F/BW blocks of the quant's block size BW),
+ * or -1 for a bad shape or quant. */
 int64_t moe_expert_bytes(int32_t hidden, int32_t ffn, int32_t quant);
 
 /* Device bytes the context holds: expert arena, routers and scratch. */
