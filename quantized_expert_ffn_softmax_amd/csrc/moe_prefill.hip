@@ -882,30 +882,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // ---------------------------------------------------------------- combine
 // Thread per (token, 4 consecutive columns): the k routed rows in slot order,
 // then the shared row, then the residual.
+template <int KM>
 __global__ __launch_bounds__(256) void k_pf_combine(const uint16_t* __restrict__ x, int T, int H, int k, int S,
                                                     PrefillBufs pb, uint16_t* __restrict__ y, int residual) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     const int h4 = H / 4;
     if (i >= T * h4) return;
     const int t = i / h4, c = (i - t * h4) * 4;
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-        const float w = pb.w[(int64_t)t * k + j];
-        const f32x4_t o = *reinterpret_cast<const f32x4_t*>(pb.o + (int64_t)pb.inv[(int64_t)t * k + j] * H + c);
+    // every row index and weight first, then every row (read once: non-temporal),
+    // so the k + 1 rows cost one memory round trip after the indices; k <= KM
+    int64_t row[KM];
+    float w[KM];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) s[q] += w * o[q];
+    for (int j = 0; j < KM; ++j) {
+        const int jj = min(j, k - 1);
+        row[j] = pb.inv[(int64_t)t * k + jj];
+        w[j] = pb.w[(int64_t)t * k + jj];
     }
-    if (S) {
-        const f32x4_t o = *reinterpret_cast<const f32x4_t*>(pb.o + ((int64_t)T * k + t) * H + c);
+    const uint32_t xv0 = *reinterpret_cast<const uint32_t*>(x + (int64_t)t * H + c);
+    const uint32_t xv1 = *reinterpret_cast<const uint32_t*>(x + (int64_t)t * H + c + 2);
+    f32x4_t o[KM];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) s[q] += o[q];
+    for (int j = 0; j < KM; ++j)
+        o[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pb.o + row[j] * H + c));
+    // the shared row exists only with S; without it the load repeats row 0's and is unused
+    const int64_t srow = S ? (int64_t)T * k + t : row[0];
+    const f32x4_t os = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pb.o + srow * H + c));
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+        if (j < k) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) s[q] += w[j] * o[j][q];
+        }
+    if (S) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s[q] += os[q];
     }
     uint32_t out[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         float a = s[2 * q], b = s[2 * q + 1];
         if (residual) {
-            const uint32_t xv = *reinterpret_cast<const uint32_t*>(x + (int64_t)t * H + c + 2 * q);
+            const uint32_t xv = q ? xv1 : xv0;
             a += bf2f(xv & 0xFFFFu);
             b += bf2f(xv >> 16);
         }
@@ -1004,7 +1023,11 @@ hipError_t launch_pf_gemm2(const uint8_t* layer_slots, const Geom& g, PrefillBuf
 
 hipError_t launch_pf_combine(const uint16_t* x, int T, const Geom& g, PrefillBufs pb, uint16_t* y, int residual,
                              const Launch& lc) {
-    launch(k_pf_combine, dim3((T * (g.H / 4) + 255) / 256), dim3(256), 0, lc, x, T, g.H, g.k, g.S, pb, y, residual);
+    const dim3 grid((T * (g.H / 4) + 255) / 256);
+    if (g.k <= 8)
+        launch(k_pf_combine<8>, grid, dim3(256), 0, lc, x, T, g.H, g.k, g.S, pb, y, residual);
+    else
+        launch(k_pf_combine<kMaxTopK>, grid, dim3(256), 0, lc, x, T, g.H, g.k, g.S, pb, y, residual);
     return hipGetLastError();
 }
 
