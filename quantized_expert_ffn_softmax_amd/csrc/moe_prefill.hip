@@ -581,43 +581,46 @@ __device__ __forceinline__ void load_bcodes(BCodes<FMT>& b, __amdgpu_buffer_rsrc
         b.sc = __builtin_amdgcn_raw_buffer_load_b64(r, offs, soff, 0);
 }
 
-__device__ __forceinline__ float ub0(uint32_t v) { return (float)(v & 0xFFu); }
-__device__ __forceinline__ float ub1(uint32_t v) { return (float)((v >> 8) & 0xFFu); }
-__device__ __forceinline__ float ub2(uint32_t v) { return (float)((v >> 16) & 0xFFu); }
-__device__ __forceinline__ float ub3(uint32_t v) { return (float)(v >> 24); }
+__device__ __forceinline__ float h16lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu)); }
+__device__ __forceinline__ float h16hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
 
-// 8 consecutive weights d*(q - o) as a bf16 B operand.  d*q is exact in fp32
-// (11 + 4 significant bits) and -o*d is exact (o a power of two), so the fma
-// is the exact weight; the pack rounds it once to bf16.
-// q4 word: nibble p (bits 4p) = element 2p, nibble p+4 (bits 16+4p) = element 2p+1.
-// The two masked words are made opaque to the compiler: it would otherwise
-// extract every nibble from w with its own v_bfe, where one v_cvt_f32_ubyteN
-// of a masked word does the extraction and the conversion at once.
-// c = -o d, exact (o a power of two), passed in like d as an fp16 value.
-__device__ __forceinline__ u32x4_t deq_q4(uint32_t w, float d, float c) {
-    uint32_t lo = w & 0x0F0F0F0Fu;         // bytes: e0 e4 e1 e5
-    uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // bytes: e2 e6 e3 e7
-    asm("" : "+v"(lo), "+v"(hi));
-    return u32x4_t{pack_bf16(fmaf(d, ub0(lo), c), fmaf(d, ub2(lo), c)),
-                   pack_bf16(fmaf(d, ub0(hi), c), fmaf(d, ub2(hi), c)),
-                   pack_bf16(fmaf(d, ub1(lo), c), fmaf(d, ub3(lo), c)),
-                   pack_bf16(fmaf(d, ub1(hi), c), fmaf(d, ub3(hi), c))};
+// 8 consecutive weights d*(q - o) as a bf16 B operand.  One and-or puts two
+// codes into an fp16 pair as 0x6400 | q = 1024 + q (exact), and one fma per
+// weight, d (1024 + q) + c with c = -(1024 + o) d, gives the exact weight:
+// c is exact in fp32 (d's 11 significant bits times 129 or 513), the product
+// is formed exactly inside the fma, and d (q - o) has at most 15 significant
+// bits.  The pack rounds it once to bf16.  v_fma_mix_f32 takes d and the
+// codes as fp16 operands (either half of a register), c as fp32.
+// kb: 0x64006400 held in a VGPR, so that the mask-and-or is one v_and_or_b32
+// (VOP3 takes at most one scalar or constant operand, which the mask uses).
+__device__ __forceinline__ uint32_t fp16_bias_bits() {
+    uint32_t k;
+    asm("v_mov_b32 %0, 0x64006400" : "=v"(k));
+    return k;
 }
-// q2 (block bits already at 0..7 and 16..23): bits 2p = element 2p, bits 16+2p = element 2p+1.
-__device__ __forceinline__ u32x4_t deq_q2(uint32_t w, float d, float c) {
+// q4 word: nibble p (bits 4p) = element 2p, nibble p+4 (bits 16+4p) = element 2p+1.
+__device__ __forceinline__ u32x4_t deq_q4(uint32_t w, float d, float c, uint32_t kb) {
     u32x4_t r;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const uint32_t v = (w >> (2 * p)) & 0x00030003u;
-        r[p] = pack_bf16(fmaf(d, ub0(v), c), fmaf(d, ub2(v), c));
+        const uint32_t v = ((w >> (4 * p)) & 0x000F000Fu) | kb;
+        r[p] = pack_bf16(fmaf(d, h16lo(v), c), fmaf(d, h16hi(v), c));
+    }
+    return r;
+}
+// q2 (block bits already at 0..7 and 16..23): bits 2p = element 2p, bits 16+2p = element 2p+1.
+__device__ __forceinline__ u32x4_t deq_q2(uint32_t w, float d, float c, uint32_t kb) {
+    u32x4_t r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t v = ((w >> (2 * p)) & 0x00030003u) | kb;
+        r[p] = pack_bf16(fmaf(d, h16lo(v), c), fmaf(d, h16hi(v), c));
     }
     return r;
 }
 // B operand of K step ks (block ks / 2: lo half for even ks, hi half for odd);
 // a dead chunk (live false) gets zero scales.
-// sc: the row's four fp16 block scales (zeroed for a dead chunk).  d and
-// c = -o d (exact: o is a power of two) enter the fma as fp16 operands,
-// converted exactly by v_fma_mix_f32; c costs one v_mul_f16 per block.
+// sc: the row's four fp16 block scales (zeroed for a dead chunk).
 // (Written with scalar halves: the same product over bit-cast f16x2 words
 // has been compiled to reuse the first word's products for the second.)
 // (q2b64: block j of 32 weights takes the scale of 64-block j / 2, in sc.x.)
@@ -627,15 +630,14 @@ template <int FMT> __device__ __forceinline__ _Float16 scale_h(u32x2_t s, int j)
     return __builtin_bit_cast(_Float16, (uint16_t)((j & 1) ? (w >> 16) : (w & 0xFFFFu)));
 }
 template <int FMT>
-__device__ __forceinline__ u32x4_t deq_half(const BCodes<FMT>& b, int ks, u32x2_t sc) {
+__device__ __forceinline__ u32x4_t deq_half(const BCodes<FMT>& b, int ks, u32x2_t sc, uint32_t kb) {
     const int j = ks >> 1;
-    const _Float16 dh = scale_h<FMT>(sc, j);
-    const _Float16 ch = dh * (_Float16)(FMT == 1 ? -8.f : -2.f);
-    const float d = (float)dh, c = (float)ch;
+    const float d = (float)scale_h<FMT>(sc, j);
+    const float c = d * (FMT == 1 ? -1032.f : -1026.f);
     if constexpr (FMT == 1) {
-        return deq_q4((ks & 1) ? b.c1[j] : b.c0[j], d, c);
+        return deq_q4((ks & 1) ? b.c1[j] : b.c0[j], d, c, kb);
     } else {
-        return deq_q2(((ks & 1) ? b.c1[j >> 1] : b.c0[j >> 1]) >> (8 * (j & 1)), d, c);
+        return deq_q2(((ks & 1) ? b.c1[j >> 1] : b.c0[j >> 1]) >> (8 * (j & 1)), d, c, kb);
     }
 }
 
@@ -704,6 +706,7 @@ __device__ __forceinline__ void gemm_item(GemmItem& it, uint8_t* As, const Geom&
     // LDS byte offset of this lane's fragment row (slice 0) and its segment swizzle
     const uint8_t* al0 = As + (lane & 31) * 256;
     const int swz = lane & 15;
+    const uint32_t kb = fp16_bias_bits();
     // chunk kc >= nk (the partner of the last chunk when nk is odd) repeats the
     // last chunk's data with zero scales: it adds exact zeros
     auto chunk = [&](int kc, int buf, const BCodes<FMT>(&cb)[2], BCodes<FMT>(&nb)[2]) {
@@ -730,8 +733,8 @@ __device__ __forceinline__ void gemm_item(GemmItem& it, uint8_t* As, const Geom&
         for (int gi = 0; gi < 2; ++gi) sc[gi] = live ? cb[gi].sc : u32x2_t{0u, 0u};
         u32x4_t afc[NS], b0c, b1c;
         read_a(0, afc);
-        b0c = deq_half<FMT>(cb[0], 0, sc[0]);
-        b1c = deq_half<FMT>(cb[1], 0, sc[1]);
+        b0c = deq_half<FMT>(cb[0], 0, sc[0], kb);
+        b1c = deq_half<FMT>(cb[1], 0, sc[1], kb);
         // issue order of this region: step 0's reads and dequantisation, then
         // per step the next step's reads followed by its MFMAs, each MFMA
         // followed by a share of the next step's dequantisation
@@ -742,8 +745,8 @@ __device__ __forceinline__ void gemm_item(GemmItem& it, uint8_t* As, const Geom&
             u32x4_t afn[NS], b0n, b1n;
             if (ks < 7) {
                 read_a(ks + 1, afn);
-                b0n = deq_half<FMT>(cb[0], ks + 1, sc[0]);
-                b1n = deq_half<FMT>(cb[1], ks + 1, sc[1]);
+                b0n = deq_half<FMT>(cb[0], ks + 1, sc[0], kb);
+                b1n = deq_half<FMT>(cb[1], ks + 1, sc[1], kb);
             }
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
@@ -899,8 +902,8 @@ __global__ __launch_bounds__(256) void k_pf_combine(const uint16_t* __restrict__
         row[j] = pb.inv[(int64_t)t * k + jj];
         w[j] = pb.w[(int64_t)t * k + jj];
     }
-    const uint32_t xv0 = *reinterpret_cast<const uint32_t*>(x + (int64_t)t * H + c);
-    const uint32_t xv1 = *reinterpret_cast<const uint32_t*>(x + (int64_t)t * H + c + 2);
+    u32x2_t xv = {0u, 0u};
+    if (residual) xv = *reinterpret_cast<const u32x2_t*>(x + (int64_t)t * H + c);
     f32x4_t o[KM];
 #pragma unroll
     for (int j = 0; j < KM; ++j)
@@ -924,9 +927,8 @@ __global__ __launch_bounds__(256) void k_pf_combine(const uint16_t* __restrict__
     for (int q = 0; q < 2; ++q) {
         float a = s[2 * q], b = s[2 * q + 1];
         if (residual) {
-            const uint32_t xv = q ? xv1 : xv0;
-            a += bf2f(xv & 0xFFFFu);
-            b += bf2f(xv >> 16);
+            a += bf2f(xv[q] & 0xFFFFu);
+            b += bf2f(xv[q] >> 16);
         }
         out[q] = f2bf(a) | (f2bf(b) << 16);
     }
