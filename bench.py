@@ -22,7 +22,10 @@ C2_q2b64 and C3_q2b64 are C2 and C3 with q2b64 experts (one fp16 scale per
 64 2-bit codes: 2.25 bits per weight, 1,382,400 bytes per expert).
 
 Timed steps replay a HIP graph of one input cycle (the eager time of the same
-steps is reported as ms_per_step_eager).
+steps is reported as ms_per_step_eager).  After the timed region, the spread
+of the step time (ms_per_step_p10_p50_p90) comes from graph replays timed one
+by one (decode: per step of each replayed cycle) or from every prefill chunk
+between events of its own.
 
 Printed: one JSON line with tokens/s, HBM GB/s on expert bytes, the roofline
 of the dominant kernel (gate/up, measured with HIP events recorded around
@@ -150,6 +153,16 @@ def main():
     ms_eager = timed_run(False)
     ms_total = timed_run(True)
     ms_per_step = ms_total / args.steps
+
+    # spread: each replay of the input cycle timed on its own (after the timed region), per step
+    n_rep = max(5, args.steps // cycle)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep + 1)]
+    evs[0].record()
+    for r in range(n_rep):
+        graph.replay()
+        evs[r + 1].record()
+    torch.cuda.synchronize()
+    spread = np.percentile([evs[r].elapsed_time(evs[r + 1]) / cycle for r in range(n_rep)], [10, 50, 90])
     tokens_per_s = T * args.steps / (ms_total / 1e3)
     log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step with graph replay of {cycle}-step "
         f"cycles, {ms_eager / args.steps * 1e3:.1f} us/step eager")
@@ -237,6 +250,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "ms_per_step_eager": round(ms_eager / args.steps, 5),
+        "ms_per_step_p10_p50_p90": [round(float(v), 5) for v in spread],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -307,6 +321,14 @@ def run_prefill(args):
     ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / steps
     log(f"[bench] timed {steps} steps: {ms_per_step:.3f} ms/step")
+    # spread: every step between events of its own (after the timed region)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        ctx.forward(x, y=y)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    spread = np.percentile([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)], [10, 50, 90])
     # profiled pass: HIP event pairs bound to each dispatch, on the launch stream
     ctx.profile_read()
     for _ in range(steps):
@@ -337,6 +359,7 @@ def run_prefill(args):
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_p10_p50_p90": [round(float(v), 4) for v in spread],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -374,7 +397,7 @@ def run_prefill(args):
         dt = time.perf_counter() - t1
         result["cpu_baseline"] = {"value": round(n / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
                                   "kind": "oracle", "sample": f"first {n} tokens of the chunk, 8 per oracle call",
-                                  "seconds": round(dt, 2)}
+                                  "seconds": round(dt, 2), **host_cpu()}
     ctx.close()
     print(json.dumps(result), flush=True)
 
@@ -428,6 +451,20 @@ def kernel_sha():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def host_cpu():
+    """The host the oracle ran on: CPU model and logical CPUs visible to the process."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(cfg, args, L, chain, T):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
     import moe_inputs as mi
@@ -465,7 +502,7 @@ def cpu_baseline(cfg, args, L, chain, T):
         n_tokens = T * calls / L  # fraction of one chain step
         sample = f"first {calls} of {L} layers of one chain step, T={T} (input generation excluded)"
     return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 2)}
+            "sample": sample, "seconds": round(dt, 2), **host_cpu()}
 
 
 if __name__ == "__main__":
