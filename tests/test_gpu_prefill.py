@@ -63,9 +63,13 @@ PF_Q4_SHARED = MoEConfig("pf_q4_shared", (1000,), 512, 256, 24, 1, 4, 2, Q4B32, 
 PF_Q2 = MoEConfig("pf_q2", (600,), 640, 160, 40, 0, 6, 1, Q2B32, mi.BIAS_ZIPF, 1.1)
 PF_ODD = MoEConfig("pf_odd", (300,), 96, 224, 7, 1, 3, 1, Q2B32, mi.BIAS_NONE, 0.0)
 PF_WIDE = MoEConfig("pf_wide", (200,), 256, 64, 1000, 0, 16, 1, Q4B32, mi.BIAS_ZIPF, 1.1)  # 16 logits per lane
+# Padded K with whole N-tiles: gate/up at H = 544 (17 blocks, F = 256: two
+# full 128-feature tiles), down at F = 352 (11 blocks, H = 512: two full tiles).
+PF_W8_K1 = MoEConfig("pf_w8_k1", (300,), 544, 256, 12, 1, 3, 1, Q4B32, mi.BIAS_NORMAL, 0.5)
+PF_W8_K2 = MoEConfig("pf_w8_k2", (300,), 512, 352, 10, 0, 2, 1, Q2B32, mi.BIAS_NONE, 0.0)
 
 
-@pytest.mark.parametrize("cfg", [PF_Q4_SHARED, PF_Q2, PF_ODD, PF_WIDE], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [PF_Q4_SHARED, PF_Q2, PF_ODD, PF_WIDE, PF_W8_K1, PF_W8_K2], ids=lambda c: c.name)
 def test_small_prefill_full_output(torch_cuda, cfg):
     from quantized_expert_ffn_softmax_amd import MoEContext
     T = cfg.T[0]
