@@ -78,7 +78,7 @@ def main():
     if args.summarize_pmc:
         return summarize_pmc(args)
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported (no collectives)"}))
+        print(json.dumps({"error": "the layer runs on one GPU: --gpus above 1 is not supported (no collectives, no sharding)"}))
         sys.exit(2)
     if args.workload == "C5":
         return run_prefill(args)

@@ -81,3 +81,14 @@ def test_binding_struct_layouts_match_the_header(tmp_path):
         assert int(got[st]) == ctypes.sizeof(cls), st
         for f in fs:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, f"{st}.{f}"
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py --gpus 2 exits with a message before touching a GPU."""
+    import json
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
