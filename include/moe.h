@@ -19,8 +19,9 @@
  *    section 二 (48 layers x 512 experts, 10 active per token).
  *  - E and k are runtime values and a wrong expert width is rejected, not
  *    reinterpreted: the first page, section 三 (items 2 and 4).
- *  - The problem statement "hidden state in, routed top-k experts, weighted
- *    FFN sum out" at fixed weights: the first page, section 六.
+ *  - The layer as a function of fixed weights (a hidden state in, the
+ *    weighted sum of its routed experts' FFN outputs out): the first page,
+ *    section 六.
  *  - The routing function, the activation and the combine rule are not on
  *    the pages.  Readings used: softmax top-k with renormalisation, bias added
  *    to the logits before selection and softmax, SwiGLU, shared expert added

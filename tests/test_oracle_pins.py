@@ -397,18 +397,21 @@ def test_rmsnorm_matches_torch_rne_and_invariants():
 
 # --------------------------------------------------------- byte accounting
 def test_byte_accounting_matches_pages():
-    # DeepSeek-V4-Flash: the Q4_K expert tensors total 145.125 GiB; q4b32 is the
-    # same 4.5 bits per weight, so 43 layers x 256 routed experts give exactly that.
+    # DeepSeek-V4-Flash ("Strata 改源码去跑 DeepSeek V4 Flash？", section 二, GGUF
+    # table): the Q4_K expert tensors total 145.125 GiB; q4b32 is the same 4.5
+    # bits per weight, so 43 layers x 256 routed experts give exactly that.
     assert 43 * 256 * C4.expert_bytes == int(145.125 * 2**30)
     assert mi.expert_bytes(4096, 2048, Q4B32) == 14_155_776
-    # Qwen3.8-Flash-Next: the fixed per-expert blob is 1,382,400 bytes = 3 x 2560 x 640
-    # weights at 2.25 bits; q2b32 spends 2.5 bits, i.e. 10/9 of the blob.
+    # Qwen3.8-Flash-Next (same page, section 三 item 4): the fixed per-expert blob
+    # is 1,382,400 bytes = 3 x 2560 x 640 weights at 2.25 bits; q2b32 spends 2.5
+    # bits, i.e. 10/9 of the blob.
     assert 3 * 2560 * 640 * 9 // 32 == 1_382_400
     assert C2.expert_bytes == 1_536_000 == 1_382_400 * 10 // 9
-    # "about 700 more experts per GB" of the 2.25-bit blob
+    # the teardown page ("Strata 引擎深度拆解", its addendum on the three-tier
+    # VRAM/RAM/NVMe layout) puts one more GB of VRAM at roughly 700 more experts
     assert int(1e9 // 1_382_400) == 723
     # q2b64 (one fp16 scale per 64 two-bit codes) is exactly the blob, and the
-    # 48 x 512 Qwen experts take the pages' "34 GB"
+    # 48 x 512 Qwen experts take the 34 GB of the Q2_0 tier (same page, section 一)
     assert C2_Q2B64.expert_bytes == C3_Q2B64.expert_bytes == 1_382_400
     assert mi.expert_bytes(2560, 640, Q2B64) == 1_382_400
     assert round(48 * 512 * C3_Q2B64.expert_bytes / 1e9) == 34
