@@ -69,7 +69,8 @@ def parse():
                         "calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     p.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "MB"),
                    help="no GPU: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a run made with "
-                        "--copy-calibration MB into profiles/gateup_traffic.json")
+                        "--copy-calibration MB into profiles/gateup_traffic.json (C2: the decode gate/up kernel) "
+                        "or profiles/gemm1_traffic.json (--workload C5: the gate/up grouped GEMM)")
     return p.parse_args()
 
 
@@ -224,14 +225,7 @@ def main():
     log(f"[bench] gate/up {gu_achieved:.0f} GB/s, down {dn_achieved:.0f} GB/s, layer {hbm_gbps:.0f} GB/s")
 
     if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        for _ in range(8):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(torch, args.copy_calibration, dev)
 
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "gateup_traffic.json")
@@ -351,6 +345,17 @@ def run_prefill(args):
     layer_tflops = (gemm1_flops + gemm2_flops + 2.0 * T * cfg.E * cfg.H) / (ms_per_step / 1e3) / 1e12
     weight_bytes = (cfg.E + cfg.S) * cfg.expert_bytes
     log(f"[bench] gemm1 {g1_tflops:.0f} TFLOP/s, gemm2 {g2_tflops:.0f} TFLOP/s, layer {layer_tflops:.0f} TFLOP/s")
+    if args.copy_calibration:
+        calibration_copy(torch, args.copy_calibration, dev)
+    # HBM bytes per gate/up GEMM launch from the committed counter summary, if
+    # it was taken on the current prefill source
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "gemm1_traffic.json")
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            tr = json.load(f)
+        if tr.get("workload") == "C5" and tr.get("kernel_sha") == kernel_sha("moe_prefill.hip"):
+            traffic = tr.get("bytes_per_launch")
     result = {
         "metric": "MoE-layer tokens/s (prefill chunk) + MFMA TFLOP/s of the grouped GEMMs",
         "value": round(T * steps / (ms_total / 1e3), 1),
@@ -379,7 +384,7 @@ def run_prefill(args):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(g1_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "avg_launch_us": round(g1_s * 1e6, 2),
             "flops_per_launch": gemm1_flops,
         },
@@ -402,15 +407,29 @@ def run_prefill(args):
     print(json.dumps(result), flush=True)
 
 
+def calibration_copy(torch, mb, dev):
+    """8 device copies of an MB-sized buffer: a stream of known size for the counters."""
+    src = torch.empty(mb << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(8):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def summarize_pmc(args):
-    """HBM traffic of the gate/up kernel from two counter runs of the same command.
+    """HBM traffic of the dominant kernel from two counter runs of the same command.
 
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what the
     same counter reads for the calibration copy (the 8 largest copy dispatches,
-    MB read and MB written each)."""
+    MB read and MB written each).  C2: the decode gate/up kernel; C5: the
+    gate/up grouped GEMM."""
     import csv
     fetch_csv, write_csv, mb = args.summarize_pmc
     calib_kib = int(mb) * 1024
+    prefill = args.workload == "C5"
+    pattern = "k_pf_gemm<1, 1>" if prefill else "k_gateup_decode"
 
     def load(path, counter):
         per = {}
@@ -419,19 +438,19 @@ def summarize_pmc(args):
                 if row.get("Counter_Name") != counter:
                     continue
                 per.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
-        gu = [v for k, vs in per.items() if "k_gateup_decode" in k for v in vs]
+        gu = [v for k, vs in per.items() if pattern in k for v in vs]
         cp = sorted((v for k, vs in per.items() if "copyBuffer" in k for v in vs), reverse=True)[:8]
         if not gu or len(cp) < 8:
-            raise SystemExit(f"{path}: {len(gu)} gate/up and {len(cp)} calibration dispatches found")
+            raise SystemExit(f"{path}: {len(gu)} {pattern} and {len(cp)} calibration dispatches found")
         return float(np.mean(gu)), float(np.mean(cp)), len(gu)
 
     f_gu, f_cp, n_f = load(fetch_csv, "FETCH_SIZE")
     w_gu, w_cp, n_w = load(write_csv, "WRITE_SIZE")
     kf, kw = calib_kib / f_cp, calib_kib / w_cp
     out = {
-        "workload": "C2",
-        "kernel": "k_gateup_decode",
-        "kernel_sha": kernel_sha(),
+        "workload": "C5" if prefill else "C2",
+        "kernel": pattern,
+        "kernel_sha": kernel_sha("moe_prefill.hip" if prefill else "moe_kernels.hip"),
         "fetch_kib_per_dispatch": round(f_gu, 1), "write_kib_per_dispatch": round(w_gu, 1),
         "dispatches": [n_f, n_w],
         "calibration_copy_MiB": int(mb),
@@ -439,15 +458,15 @@ def summarize_pmc(args):
         "scale_fetch": round(kf, 4), "scale_write": round(kw, 4),
         "bytes_per_launch": round((f_gu * kf + w_gu * kw) * 1024, 1),
     }
-    path = os.path.join(ROOT, "profiles", "gateup_traffic.json")
+    path = os.path.join(ROOT, "profiles", "gemm1_traffic.json" if prefill else "gateup_traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
 
-def kernel_sha():
+def kernel_sha(source="moe_kernels.hip"):
     import hashlib
-    with open(os.path.join(ROOT, "quantized_expert_ffn_softmax_amd", "csrc", "moe_kernels.hip"), "rb") as f:
+    with open(os.path.join(ROOT, "quantized_expert_ffn_softmax_amd", "csrc", source), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
