@@ -212,3 +212,38 @@ def test_long_chunk_many_sort_blocks(torch_cuda):
     with MoEContext.from_config(cfg, max_tokens=12000) as ctx:
         W, b, ex = load_layer(ctx, cfg, 13, 0)
         _check_full(ctx, cfg, 13, 0, 0, 12000, W, b, ex, "long/T12000")
+
+
+def test_max_sizes_chunk(torch_cuda):
+    """The largest call the boundary accepts in every dimension at once: a
+    65,536-token chunk (max_tokens), hidden 4096, FF 2048, top-16, a shared
+    expert (1.1M sorted rows; o alone is 18 GB), so every 64-bit offset and the
+    tile list run at their limits.  Routing and y on sampled tokens (the
+    first, the last and 24 seeded ones); y finite and non-zero everywhere."""
+    import torch
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    cfg = MoEConfig("pf_max", (65536,), 4096, 2048, 64, 1, 16, 1, Q4B32, mi.BIAS_NORMAL, 0.5)
+    T = 65536
+    with MoEContext.from_config(cfg, max_tokens=T) as ctx:
+        W, b, ex = load_layer(ctx, cfg, 21, 0)
+        x = mi.gen_x(21, 0, T, cfg.H)
+        xd = to_dev_bf16(x)
+        print(f"[prefill] max sizes: T={T} H={cfg.H} F={cfg.F} E={cfg.E}+{cfg.S} k={cfg.k}", flush=True)
+        ids, w, offsets, perm = ctx.route(0, xd)
+        y = ctx.forward(xd)
+        torch.cuda.synchronize()
+        off = offsets.cpu().numpy()
+        assert off[0] == 0 and off[-1] == T * cfg.k and (np.diff(off) >= 0).all()
+        pm = perm.cpu().numpy()
+        assert np.array_equal(np.sort(pm), np.arange(T * cfg.k))
+        rng = np.random.default_rng(21)
+        sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 24, replace=False)]))
+        y_ref, ids_s, w_s, _ = oracle.moe_layer(np.ascontiguousarray(x[sample]), cfg.H, cfg.F, cfg.E, cfg.S, cfg.k,
+                                                cfg.fmt, W, b, ex, cfg.expert_bytes)
+        np.testing.assert_array_equal(ids.cpu().numpy()[sample], ids_s)
+        assert np.abs(w.cpu().numpy()[sample].astype(np.float64) - w_s).max() <= W_TOL
+        yg = bf16_dev_to_f64(y)
+        r, mx = assert_y_close(yg[sample], y_ref, "max sizes sampled")
+        print(f"[prefill] max sizes: sampled rel-L2 {r:.2e} max-abs {mx:.2e}", flush=True)
+        assert np.isfinite(yg).all()
+        assert (np.abs(yg).max(axis=1) > 0).all()
