@@ -212,6 +212,9 @@ def test_create_rejects_bad_geometry(torch_cuda):
 # shared expert, an 8-token window (128 pairs, up to 129 active experts),
 # hidden 4096 (two 16-byte segments per lane in the router).
 MAX_DECODE = MoEConfig("max_decode", (8,), 4096, 64, 1024, 1, 16, 1, Q2B32, mi.BIAS_ZIPF, 0.3)
+# the largest expert (hidden 4096, FF 2048, q4b32) with top-16 and a shared
+# expert: up to 129 active experts of 14.2 MB in one window of 8
+MAX_FFN_DECODE = MoEConfig("max_ffn_decode", (8,), 4096, 2048, 256, 1, 16, 1, Q4B32, mi.BIAS_NORMAL, 0.5)
 
 
 @pytest.mark.parametrize("T", [1, 4, 8])
@@ -221,3 +224,12 @@ def test_decode_at_the_size_limits(torch_cuda, T):
     with MoEContext.from_config(cfg) as ctx:
         W, b, ex = load_layer(ctx, cfg, 12, 0)
         _check_layer(ctx, cfg, 12, 0, T, T, W, b, ex, f"max_decode/T{T}")
+
+
+def test_decode_largest_experts_top16(torch_cuda):
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    cfg = MAX_FFN_DECODE
+    with MoEContext.from_config(cfg) as ctx:
+        W, b, ex = load_layer(ctx, cfg, 14, 0)
+        for T in (4, 8):
+            _check_layer(ctx, cfg, 14, 0, T, T, W, b, ex, f"max_ffn_decode/T{T}")
