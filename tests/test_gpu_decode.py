@@ -233,3 +233,29 @@ def test_decode_largest_experts_top16(torch_cuda):
         W, b, ex = load_layer(ctx, cfg, 14, 0)
         for T in (4, 8):
             _check_layer(ctx, cfg, 14, 0, T, T, W, b, ex, f"max_ffn_decode/T{T}")
+
+
+def test_two_contexts_interleaved(torch_cuda):
+    """Two live contexts of different geometry and format (and a prefill-capable
+    one) used in turn on one stream: each call matches the oracle and repeats its
+    own first result bit for bit, so no state leaks between contexts."""
+    import torch
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    a_cfg, b_cfg = SMALL_Q4_SHARED, SMALL_Q2
+    with MoEContext.from_config(a_cfg, max_tokens=64) as ca, MoEContext.from_config(b_cfg) as cb:
+        a_in = load_layer(ca, a_cfg, 17, 0)
+        b_in = load_layer(cb, b_cfg, 18, 0)
+        first = {}
+        for rnd in range(2):
+            for name, ctx, cfg, inp, T in (("a4", ca, a_cfg, a_in, 4), ("b8", cb, b_cfg, b_in, 8),
+                                            ("a40", ca, a_cfg, a_in, 40), ("b3", cb, b_cfg, b_in, 3)):
+                x = mi.gen_x(19, 0, T, cfg.H)
+                y = ctx.forward(to_dev_bf16(x))
+                torch.cuda.synchronize()
+                bits = bf16_dev_to_bits(y)
+                if rnd == 0:
+                    first[name] = bits
+                    y_ref = oracle.moe_layer(x, cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, cfg.fmt, *inp, cfg.expert_bytes)[0]
+                    assert_y_close(bf16_dev_to_f64(y), y_ref, f"two contexts/{name}")
+                else:
+                    np.testing.assert_array_equal(bits, first[name], err_msg=f"two contexts/{name} repeat")
