@@ -523,6 +523,9 @@ __global__ __launch_bounds__(256) void k_pf_scatter(int T, int E, int k, int S, 
 // segment hit 16 distinct bank groups.
 constexpr int kATileBytes = 128 * 256;
 constexpr int kGemmLds = 2 * kATileBytes;  // double buffer
+// VALU instructions of one K step's dequantisation (two B operands), spread
+// over the step's MFMAs by the scheduling groups
+constexpr int kDeqValu = 40;
 
 // Work item of block b.  Workgroups are dealt to the 8 XCDs round-robin, so
 // block b runs on XCD x = b % 8 as its slot s = b / 8 there.  M-blocks are
@@ -739,7 +742,7 @@ __device__ __forceinline__ void gemm_item(GemmItem& it, uint8_t* As, const Geom&
         // per step the next step's reads followed by its MFMAs, each MFMA
         // followed by a share of the next step's dequantisation
         __builtin_amdgcn_sched_group_barrier(0x100, NS, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 56, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kDeqValu, 0);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             u32x4_t afn[NS], b0n, b1n;
@@ -763,7 +766,7 @@ __device__ __forceinline__ void gemm_item(GemmItem& it, uint8_t* As, const Geom&
 #pragma unroll
             for (int i = 0; i < 2 * NS; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, (56 + 2 * NS - 1) / (2 * NS), 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, (kDeqValu + 2 * NS - 1) / (2 * NS), 0);
             }
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): chunk kc + 1 has landed
