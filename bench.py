@@ -21,11 +21,12 @@ and the roofline is that of the gate/up grouped GEMM on bf16 MFMA.
 C2_q2b64 and C3_q2b64 are C2 and C3 with q2b64 experts (one fp16 scale per
 64 2-bit codes: 2.25 bits per weight, 1,382,400 bytes per expert).
 
-Timed steps replay a HIP graph of one input cycle (the eager time of the same
-steps is reported as ms_per_step_eager).  After the timed region, the spread
-of the step time (ms_per_step_p10_p50_p90) comes from graph replays timed one
-by one (decode: per step of each replayed cycle) or from every prefill chunk
-between events of its own.
+Decode: the timed steps replay a HIP graph, of one input cycle when the step
+count is a multiple of it and of exactly the timed steps otherwise; the eager
+time of the same steps is reported as ms_per_step_eager.  After the timed
+region, the spread of the step time (ms_per_step_p10_p50_p90) comes from
+further replays of the same graph, each timed on its own (per step), or, for
+the prefill chunk, from every chunk between events of its own.
 
 Printed: one JSON line with tokens/s, HBM GB/s on expert bytes, the roofline
 of the dominant kernel (gate/up, measured with HIP events recorded around
@@ -117,56 +118,59 @@ def main():
         moe_forward(ctx.handle, xs[i % len(xs)], y, T, layer, 1, MOE_FWD_PROFILE if profile else 0,
                     None, trace_ids, None)
 
-    # ---- warmup + timed region (no profiling events).  Decode steps are launch-bound, so the timed steps
-    #      replay a HIP graph that holds one full input cycle (every resident layer and window once); a
-    #      remainder of steps runs eagerly, so exactly `steps` steps are timed.  The eager time of the same
-    #      steps is reported beside it.
+    # ---- warmup, then the same steps eagerly (reported beside) and as HIP graph replays (the timed value).
+    #      Decode steps are launch-bound, so the timed steps replay a HIP graph: of one full input cycle
+    #      (every resident layer and window once) when the step count is a multiple of it, else of exactly
+    #      the timed steps.  The spread after the timed region comes from further replays of the same graph.
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     cycle = len(xs) if chain else int(np.lcm(L, len(xs)))
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        graph.capture_begin()
-        for i in range(cycle):
-            step(i)
-        graph.capture_end()
-    torch.cuda.current_stream().wait_stream(side)
-    graph.replay()
-    torch.cuda.synchronize()
+    gsteps = cycle if args.steps % cycle == 0 else args.steps
+    replays = args.steps // gsteps
 
-    def timed_run(use_graph):
+    def timed_eager():
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record()
-        done = 0
-        if use_graph:
-            while done + cycle <= args.steps:
-                graph.replay()
-                done += cycle
-        for i in range(done, args.steps):
+        for i in range(args.steps):
             step(i)
         ev1.record()
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1)
 
-    ms_eager = timed_run(False)
-    ms_total = timed_run(True)
+    ms_eager = timed_eager()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        graph.capture_begin()
+        for i in range(gsteps):
+            step(i)
+        graph.capture_end()
+    torch.cuda.current_stream().wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(replays):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / args.steps
 
-    # spread: each replay of the input cycle timed on its own (after the timed region), per step
-    n_rep = max(5, args.steps // cycle)
+    # spread: further replays of the same graph, each timed on its own, per step
+    n_rep = max(5, replays)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep + 1)]
     evs[0].record()
     for r in range(n_rep):
         graph.replay()
         evs[r + 1].record()
     torch.cuda.synchronize()
-    spread = np.percentile([evs[r].elapsed_time(evs[r + 1]) / cycle for r in range(n_rep)], [10, 50, 90])
+    spread = np.percentile([evs[r].elapsed_time(evs[r + 1]) / gsteps for r in range(n_rep)], [10, 50, 90])
     tokens_per_s = T * args.steps / (ms_total / 1e3)
-    log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step with graph replay of {cycle}-step "
-        f"cycles, {ms_eager / args.steps * 1e3:.1f} us/step eager")
+    log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step as {replays} replay(s) of a "
+        f"{gsteps}-step HIP graph, {ms_eager / args.steps * 1e3:.1f} us/step eager")
 
     # ---- routing of every (layer, window) pair used: distinct experts -> algorithmic bytes
     n_pairs = L if chain else int(np.lcm(L, len(xs)))
@@ -256,7 +260,7 @@ def main():
                                                   f"{L}-layer MoE-only decode chain with residual per step")),
             "T": T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "S": cfg.S, "k": cfg.k, "layers_resident": L,
             "quant": {1: "q4b32", 2: "q2b32", 3: "q2b64"}[cfg.fmt], "seed": args.seed,
-            "launch": f"HIP graph replay of {cycle}-step cycles",
+            "launch": f"{replays} replay(s) of a HIP graph of {gsteps} steps (captured by the caller)",
         },
         "hbm_GBps": round(hbm_gbps, 1),
         "hbm_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
@@ -471,57 +475,93 @@ def kernel_sha(source="moe_kernels.hip"):
 
 
 def host_cpu():
-    """The host the oracle ran on: CPU model and logical CPUs visible to the process."""
+    """The host the oracle ran on: CPU model, logical CPUs visible to the process, and the physical cores
+    among them (distinct (physical id, core id) pairs of /proc/cpuinfo)."""
     model = ""
+    cores = set()
+    visible = os.sched_getaffinity(0)
     try:
         with open("/proc/cpuinfo") as f:
+            proc = phys = None
             for line in f:
-                if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "processor":
+                    proc, phys = int(val), None
+                elif key == "model name" and not model:
+                    model = val
+                elif key == "physical id":
+                    phys = val
+                elif key == "core id" and proc in visible:
+                    cores.add((phys, val))
     except OSError:
         pass
-    return {"cpu_model": model, "nproc": len(os.sched_getaffinity(0))}
+    return {"cpu_model": model, "nproc": len(visible), "physical_cores": len(cores) or None}
+
+
+def _time_layer_calls(cfg, W, b, ex, xs, budget_s, max_calls):
+    """Oracle layer calls on pre-generated windows (input generation outside the timed calls)."""
+    import oracle
+    calls = 0
+    t = 0.0
+    while t < budget_s and calls < max_calls:
+        x = xs[calls % len(xs)]
+        t1 = time.perf_counter()
+        oracle.moe_layer(x, cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, cfg.fmt, W, b, ex, cfg.expert_bytes)
+        t += time.perf_counter() - t1
+        calls += 1
+    return calls, t
 
 
 def cpu_baseline(cfg, args, L, chain, T):
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload; single-layer workloads are
+    also timed on one thread (and the tiny 4-token layer beside them)."""
     import moe_inputs as mi
     import oracle
+    from moe_inputs.configs import C1
     threads = oracle.num_threads()
-    t_start = time.perf_counter()
-    n_tokens = 0
-    calls = 0
+    extra = {}
     if not chain:
         W, b, ex = mi.layer_inputs(cfg, args.seed, 0)
-        t_start = time.perf_counter()
-        while time.perf_counter() - t_start < args.cpu_seconds and calls < 256:
-            x = mi.gen_x(args.seed, calls % args.windows, T, cfg.H)
-            oracle.moe_layer(x, cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, cfg.fmt, W, b, ex, cfg.expert_bytes)
-            n_tokens += T
-            calls += 1
-        dt = time.perf_counter() - t_start
-        sample = f"{calls} calls of layer 0 on {T}-token windows (input generation excluded)"
+        xs = [mi.gen_x(args.seed, w, T, cfg.H) for w in range(args.windows)]
+        calls, dt = _time_layer_calls(cfg, W, b, ex, xs, args.cpu_seconds, 256)
+        n_tokens = T * calls
+        sample = f"{calls} calls of layer 0 on {T}-token windows (inputs generated before timing)"
+        # one thread: the same layer, and the tiny layer (hidden 256, 16 experts, top-2, 4 tokens)
+        oracle.set_num_threads(1)
+        try:
+            c1, d1 = _time_layer_calls(cfg, W, b, ex, xs, min(4.0, args.cpu_seconds / 3), 64)
+            W1, b1, ex1 = mi.layer_inputs(C1, 1, 0)
+            x1 = [mi.gen_x(1, w, 4, C1.H) for w in range(4)]
+            cc1, dd1 = _time_layer_calls(C1, W1, b1, ex1, x1, 1.0, 4096)
+        finally:
+            oracle.set_num_threads(threads)
+        extra = {"single_thread": {"value": round(T * c1 / d1, 3), "unit": "tokens/s", "calls": c1,
+                                   "seconds": round(d1, 2)},
+                 "tiny_layer_C1": {"tokens_per_s_all_threads": None, "tokens_per_s_single_thread":
+                                   round(4 * cc1 / dd1, 1), "calls": cc1}}
+        cA, dA = _time_layer_calls(C1, W1, b1, ex1, x1, 1.0, 4096)
+        extra["tiny_layer_C1"]["tokens_per_s_all_threads"] = round(4 * cA / dA, 1)
     else:
         # a chain step needs every layer; time the layers one by one and extrapolate nothing:
         # the sample is the first layers of one chain step
         x = mi.gen_x(args.seed, 0, T, cfg.H)
-        t_layers = 0.0
+        dt = 0.0
+        calls = 0
         for layer in range(L):
             W, b, ex = mi.layer_inputs(cfg, args.seed, layer)
             t1 = time.perf_counter()
             y, *_ = oracle.moe_layer(oracle.rmsnorm_bf16(x), cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, cfg.fmt, W, b, ex,
                                      cfg.expert_bytes)
             x = oracle.residual_bf16(x, y)
-            t_layers += time.perf_counter() - t1
+            dt += time.perf_counter() - t1
             calls += 1
-            if t_layers > args.cpu_seconds:
+            if dt > args.cpu_seconds:
                 break
-        dt = t_layers
         n_tokens = T * calls / L  # fraction of one chain step
         sample = f"first {calls} of {L} layers of one chain step, T={T} (input generation excluded)"
     return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 2), **host_cpu()}
+            "sample": sample, "seconds": round(dt, 2), **host_cpu(), **extra}
 
 
 if __name__ == "__main__":

@@ -68,6 +68,8 @@ def lib():
         L.oracle_rmsnorm_bf16.restype = None
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = i32
+        L.oracle_set_num_threads.argtypes = [i32]
+        L.oracle_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -75,6 +77,11 @@ def lib():
 def num_threads() -> int:
     """OpenMP threads used by the oracle's parallel loops."""
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's later parallel loops (timing only; results do not depend on it)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def _p(a):
@@ -218,17 +225,3 @@ def rmsnorm_bf16(x_bits: np.ndarray, eps: float = RMSNORM_EPS) -> np.ndarray:
         lib().oracle_rmsnorm_bf16(_p(x[t]), x.shape[1], eps, _p(out[t]))
     return out.reshape(np.shape(x_bits))
 
-
-def chain(x_bits, cfg, seed, layer_inputs_fn, n_layers):
-    """Oracle chain of n_layers MoE layers with the bf16 residual between them.
-
-    layer_inputs_fn(layer) -> (W_bits, bias, experts).  Returns the list of
-    per-layer (x_in_bits, y, ids, w, logits)."""
-    out = []
-    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
-    for layer in range(n_layers):
-        W, b, ex = layer_inputs_fn(layer)
-        y, ids, w, lg = moe_layer(x, cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, cfg.fmt, W, b, ex, cfg.expert_bytes)
-        out.append((x.copy(), y, ids, w, lg))
-        x = residual_bf16(x, y)
-    return out, x

@@ -367,3 +367,6 @@ int oracle_num_threads(void) {
     }
     return n;
 }
+
+/* Threads for the oracle's later parallel loops (a timing knob, no arithmetic). */
+void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }

@@ -56,3 +56,23 @@ def load_layer(ctx, cfg, seed, layer, raw=False, staging_experts=None):
     W, b, ex = mi.layer_inputs(cfg, seed, layer, raw=raw)
     ctx.load(layer, router_w=W, router_bias=b, experts=ex)
     return W, b, ex
+
+
+def oracle_layer_selected(x_bits, cfg, seed, layer, W, b, raw=False):
+    """The oracle's layer output on x_bits with only the experts it selects
+    (and the shared expert) generated: the same seeded bytes as the full
+    layer, since every expert's bytes are keyed by (seed, layer, expert).
+    Returns (y [T x H] float64, ids [T x k], w [T x k])."""
+    import oracle
+    ids, w = oracle.select_topk(oracle.router_logits(x_bits, W, b), cfg.k)
+    uniq = np.unique(ids)
+    remap = np.full(cfg.E, -1, dtype=np.int32)
+    remap[uniq] = np.arange(len(uniq), dtype=np.int32)
+    eb = cfg.expert_bytes
+    ex = np.empty((len(uniq) + cfg.S) * eb, dtype=np.uint8)
+    for i, e in enumerate(uniq):
+        mi.gen_experts(seed, layer, int(e), 1, cfg.H, cfg.F, cfg.fmt, raw=raw, out=ex[i * eb:(i + 1) * eb])
+    if cfg.S:
+        mi.gen_experts(seed, layer, cfg.E, 1, cfg.H, cfg.F, cfg.fmt, raw=raw, out=ex[len(uniq) * eb:])
+    y = oracle.combine(x_bits, cfg.H, cfg.F, len(uniq), cfg.S, cfg.k, cfg.fmt, remap[ids], w, ex, eb)
+    return y, ids, w

@@ -10,13 +10,15 @@ by layer 21, bf16 overflow at 22), and nothing past the first tens of layers
 could be checked or timed.
 
 Teacher forcing: each layer is judged on the GPU's own bf16 MoE input, taken
-from trace_x.  Per layer the routing (ids, weights) must match the oracle
-bit-exactly / within 1e-6, the pre-norm must match the oracle's within one
-bf16 unit in the last place, the chain must equal the composition of
-single-layer calls bit for bit, and on sampled layers the layer output must
-match the oracle within the rel-L2 / max-abs bar.  The drift of the
-end-to-end output against an fp64 oracle chain (bf16 rounding at the same
-points) is printed, not gated.
+from trace_x.  Per layer, at every window: the routing (ids, weights) must
+match the oracle bit-exactly / within 1e-6, the pre-norm must match the
+oracle's within one bf16 unit in the last place, the chain must equal the
+composition of single-layer calls bit for bit, and the layer output y_l (a
+single-layer call on the traced input, no residual) must match the oracle's
+within the rel-L2 / max-abs bar over the whole [T x H] output.  The oracle
+generates only the experts it selects (the same seeded bytes as the full
+layer).  The drift of the end-to-end output against an fp64 oracle chain
+(bf16 rounding at the same points) is printed, not gated.
 """
 import numpy as np
 import pytest
@@ -25,7 +27,8 @@ import moe_inputs as mi
 import oracle
 from moe_inputs.configs import C3, C4
 
-from parity import W_TOL, assert_y_close, bf16_dev_to_bits, bf16_dev_to_f64, rel_l2, to_dev_bf16
+from parity import (W_TOL, assert_y_close, bf16_dev_to_bits, bf16_dev_to_f64, oracle_layer_selected, rel_l2,
+                    to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,37 +72,29 @@ def _check_chain(ctx, cfg, routers, T):
     w_all = tw.cpu().numpy().astype(np.float64)
     x = x0
     worst_norm = 0
+    worst = (0.0, 0.0)
     for layer in range(cfg.L):
         W, b = routers[layer]
-        ids_ref, w_ref = oracle.select_topk(oracle.router_logits(thb[layer], W, b), cfg.k)
-        np.testing.assert_array_equal(ids_all[layer], ids_ref, err_msg=f"{cfg.name} T={T} layer {layer}: ids")
-        assert np.abs(w_all[layer] - w_ref).max() <= W_TOL, f"{cfg.name} T={T} layer {layer}: weights"
+        what = f"{cfg.name} T={T} layer {layer}"
+        y_ref, ids_ref, w_ref = oracle_layer_selected(thb[layer], cfg, SEED, layer, W, b)
+        np.testing.assert_array_equal(ids_all[layer], ids_ref, err_msg=f"{what}: ids")
+        assert np.abs(w_all[layer] - w_ref).max() <= W_TOL, f"{what}: weights"
         worst_norm = max(worst_norm, int(_ulp_diff(thb[layer], oracle.rmsnorm_bf16(x)).max()))
         # the chain is the composition of single-layer calls, bit for bit
         xn, th1, _, _ = ctx.forward(to_dev_bf16(x), layer, 1, residual=True, trace=True, prenorm=True)
+        # the layer output on the traced input (no pre-norm, no residual) against the oracle's
+        yl = ctx.forward(to_dev_bf16(thb[layer]), layer, 1)
         torch.cuda.synchronize()
-        np.testing.assert_array_equal(bf16_dev_to_bits(th1)[0], thb[layer],
-                                      err_msg=f"{cfg.name} T={T} layer {layer}: pre-norm of the chain")
+        np.testing.assert_array_equal(bf16_dev_to_bits(th1)[0], thb[layer], err_msg=f"{what}: pre-norm of the chain")
+        r, mx = assert_y_close(bf16_dev_to_f64(yl), y_ref, what)
+        worst = (max(worst[0], r), max(worst[1], mx / float(np.abs(y_ref).max())))
         x = bf16_dev_to_bits(xn)
     np.testing.assert_array_equal(x, bf16_dev_to_bits(y), err_msg=f"{cfg.name} T={T}: chain output")
     assert worst_norm <= 1, f"{cfg.name} T={T}: pre-norm differs from the oracle's by {worst_norm} ulp"
     rms = float(np.sqrt((oracle.bf16_to_f64(x) ** 2).mean()))
-    print(f"[chain] {cfg.name} T={T}: routing of {cfg.L} layers exact, chain = composition, pre-norm within "
-          f"{worst_norm} ulp, final stream rms {rms:.2f}", flush=True)
-    return thb
-
-
-def _check_sampled_outputs(ctx, cfg, txb, layers):
-    import torch
-    for layer in layers:
-        W, b, ex = mi.layer_inputs(cfg, SEED, layer)
-        yg = ctx.forward(to_dev_bf16(txb[layer]), layer, 1)
-        torch.cuda.synchronize()
-        y_ref, _, _, _ = oracle.moe_layer(txb[layer], cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, cfg.fmt, W, b, ex,
-                                          cfg.expert_bytes)
-        r, mx = assert_y_close(bf16_dev_to_f64(yg), y_ref, f"{cfg.name} layer {layer}")
-        print(f"[chain] {cfg.name} layer {layer} (teacher-forced): rel-L2 {r:.2e} max-abs {mx:.2e}", flush=True)
-        del ex
+    print(f"[chain] {cfg.name} T={T}: routing and y of all {cfg.L} layers match (worst rel-L2 {worst[0]:.2e}, "
+          f"worst max-abs {worst[1]:.2e} of max|ref|), chain = composition, pre-norm within {worst_norm} ulp, "
+          f"final stream rms {rms:.2f}", flush=True)
 
 
 def test_qwen_chain_48_layers(torch_cuda):
@@ -109,8 +104,7 @@ def test_qwen_chain_48_layers(torch_cuda):
     with MoEContext.from_config(cfg, max_tokens=8) as ctx:
         routers = _load_chain(ctx, cfg)
         for T in (1, 4, 8):
-            txb = _check_chain(ctx, cfg, routers, T)
-        _check_sampled_outputs(ctx, cfg, txb, [0, cfg.L // 2, cfg.L - 1])
+            _check_chain(ctx, cfg, routers, T)
 
 
 def test_deepseek_chain_43_layers(torch_cuda):
@@ -120,8 +114,7 @@ def test_deepseek_chain_43_layers(torch_cuda):
     with MoEContext.from_config(cfg, max_tokens=8) as ctx:
         routers = _load_chain(ctx, cfg)
         for T in (1, 4, 8):
-            txb = _check_chain(ctx, cfg, routers, T)
-        _check_sampled_outputs(ctx, cfg, txb, [0, cfg.L - 1])
+            _check_chain(ctx, cfg, routers, T)
 
 
 def test_qwen_chain_end_to_end_drift_report(torch_cuda):

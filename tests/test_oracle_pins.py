@@ -425,3 +425,20 @@ def test_c5_zipf_calibration_fixture():
     assert rec["max_tokens_per_expert"] > 500
     assert rec["previous_s_max"] <= 500
     assert sum(rec["histogram"]) == 4096 * 6
+
+
+def test_selected_experts_helper_equals_full_layer():
+    """The parity helper that generates only the selected experts (and the
+    shared one) gives the full-layer oracle's output bit for bit."""
+    from moe_inputs.configs import MoEConfig, Q2B32, Q4B32
+    from parity import oracle_layer_selected
+    for cfg in (MoEConfig("sel_q4s", (5,), 256, 96, 24, 1, 4, 3, Q4B32, mi.BIAS_NORMAL, 0.5),
+                MoEConfig("sel_q2", (3,), 320, 64, 40, 0, 6, 2, Q2B32, mi.BIAS_ZIPF, 1.1)):
+        for layer in range(cfg.L):
+            W, b, ex = mi.layer_inputs(cfg, 4, layer)
+            x = mi.gen_x(4, layer, cfg.T[0], cfg.H)
+            y, ids, w, _ = oracle.moe_layer(x, cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, cfg.fmt, W, b, ex, cfg.expert_bytes)
+            y2, ids2, w2 = oracle_layer_selected(x, cfg, 4, layer, W, b)
+            np.testing.assert_array_equal(ids2, ids)
+            np.testing.assert_array_equal(w2, w)
+            np.testing.assert_array_equal(y2, y)
