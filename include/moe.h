@@ -232,6 +232,30 @@ typedef struct {
  * forgets all recorded launches.  Profiling keeps at most 65536 launches. */
 moe_status moe_profile_read(moe_ctx* ctx, moe_kernel_time* out, int32_t cap, int32_t* n_out);
 
+/* moe_route_static: routing of one decode window (steps 1-3 above, score
+ * routing, no shared expert) on caller-owned router weights, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It needs no context and calls no
+ * allocating routine; its scratch (fp64 logits, per-block sums of x, inverse
+ * permutation, active list) is one file-scope device array of 96 KiB per GPU,
+ * held until the process ends, whose address is looked up once per device on
+ * the first call made with that device current.  The same kernels as
+ * moe_route for T <= 8 run on the stream passed in, so the results are those
+ * of moe_route on a context holding the same router.
+ *   x        : [T x H] bf16, device, 16-byte aligned
+ *   T        : 0..8 (MOE_ERANGE above; 0 is a no-op)
+ *   hidden   : H, positive multiple of 32, at most 4096
+ *   n_experts: E, 1..1024;  top_k: k in [1, min(E, 16)]
+ *   router_w : [E x H] bf16, device, 16-byte aligned;  router_bias: [E] fp32, device, or NULL
+ *   ids, w   : [T x k], device (as moe_route);  offsets [E+1], perm [T*k]: device or NULL
+ * MOE_ERANGE when the scratch for (E, k, H) would exceed the array (it never
+ * does within the limits above).  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (two streams, two host threads) race;
+ * order them on one stream. */
+moe_status moe_route_static(const void* x, int32_t T, int32_t hidden, int32_t n_experts, int32_t top_k,
+                            const void* router_w, const float* router_bias, int32_t* ids, float* w, int32_t* offsets,
+                            int32_t* perm, void* hip_stream);
+
 /* Canonical bytes of one expert (3*H*F/BW blocks of the quant's block size BW),
  * or -1 for a bad shape or quant. */
 int64_t moe_expert_bytes(int32_t hidden, int32_t ffn, int32_t quant);

@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOMEM", -3: "MOE_EHIP",
 
 # Every symbol include/moe.h declares.
 EXPORTED = ("moe_create", "moe_load_experts", "moe_route", "moe_forward", "moe_destroy", "moe_last_error",
-            "moe_expert_bytes", "moe_memory_bytes", "moe_profile_read")
+            "moe_expert_bytes", "moe_memory_bytes", "moe_profile_read", "moe_route_static")
 
 
 class moe_config(ctypes.Structure):
@@ -82,8 +82,9 @@ def lib():
         L.moe_expert_bytes.restype = ctypes.c_int64
         L.moe_memory_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)]
         L.moe_profile_read.argtypes = [vp, ctypes.POINTER(moe_kernel_time), i32, ctypes.POINTER(i32)]
+        L.moe_route_static.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
         for f in ("moe_create", "moe_load_experts", "moe_route", "moe_forward", "moe_destroy", "moe_memory_bytes",
-                  "moe_profile_read"):
+                  "moe_profile_read", "moe_route_static"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -143,6 +144,14 @@ def moe_load_experts(ctx, layer, router_w=None, router_bias=None, experts=None, 
 def moe_route(ctx, layer, x, T, ids, w, offsets=None, perm=None, stream=None, token_ids=None):
     _check(lib().moe_route(ctx, layer, _dptr(x), T, _dptr(token_ids), _dptr(ids), _dptr(w), _dptr(offsets),
                            _dptr(perm), _stream(stream)))
+
+
+def moe_route_static(x, T, hidden, n_experts, top_k, router_w, router_bias, ids, w, offsets=None, perm=None,
+                     stream=None):
+    """Decode-window routing on device router weights with the library's static scratch (no context, no
+    allocation)."""
+    _check(lib().moe_route_static(_dptr(x), T, hidden, n_experts, top_k, _dptr(router_w), _dptr(router_bias),
+                                  _dptr(ids), _dptr(w), _dptr(offsets), _dptr(perm), _stream(stream)))
 
 
 def moe_forward(ctx, x, y, T, layer_begin=0, layer_count=1, flags=0, trace_x=None, trace_ids=None, trace_w=None,

@@ -15,6 +15,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -599,6 +600,105 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
         if (s != MOE_OK) return s;
         xin = yout;
     }
+    return MOE_OK;
+}
+
+// ---------------------------------------------------------------- routing without allocation
+// moe_route_static: the decode-window routing kernels of moe_route (router
+// GEMV, top-k, weights, counting sort) on caller-owned router weights, with
+// their scratch (fp64 logits, per-block sums of x, inverse permutation, active
+// list, weight table) in one file-scope device array per GPU instead of a
+// context.  hipGetSymbolAddress gives each device's own address of the array
+// once, on the first call made with that device current; kernels only ever
+// receive that address.
+namespace {
+constexpr size_t kStaticScratchBytes = 96u << 10;
+constexpr int kStaticMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kStaticMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+// Carves RouteBufs for T <= 8 tokens and E experts out of the array at base;
+// returns the bytes used.
+size_t carve_static_route(uint8_t* base, int E, int k, int H, RouteBufs* rb) {
+    Carver cv;
+    const int nbHp = (H / 32 + kChunkBlocks - 1) / kChunkBlocks * kChunkBlocks;
+    const int maxA = std::min(E, kMaxDecodeT * k);
+    const size_t o_logits = cv.take<double>((size_t)kMaxDecodeT * E);
+    const size_t o_sx = cv.take<float>((size_t)nbHp * 16);
+    const size_t o_ids = cv.take<int32_t>((size_t)kMaxDecodeT * k);
+    const size_t o_w = cv.take<float>((size_t)kMaxDecodeT * k);
+    const size_t o_off = cv.take<int32_t>((size_t)E + 1);
+    const size_t o_perm = cv.take<int32_t>((size_t)kMaxDecodeT * k);
+    const size_t o_inv = cv.take<int32_t>((size_t)kMaxDecodeT * k);
+    const size_t o_nact = cv.take<int32_t>(1);
+    const size_t o_act = cv.take<int32_t>((size_t)maxA);
+    const size_t o_wtab = cv.take<float>((size_t)maxA * kMaxDecodeT);
+    if (rb && base) {
+        rb->logits = (double*)(base + o_logits);
+        rb->sx = (float*)(base + o_sx);
+        rb->ids = (int32_t*)(base + o_ids);
+        rb->w = (float*)(base + o_w);
+        rb->offsets = (int32_t*)(base + o_off);
+        rb->perm = (int32_t*)(base + o_perm);
+        rb->inv = (int32_t*)(base + o_inv);
+        rb->nact = (int32_t*)(base + o_nact);
+        rb->act = (int32_t*)(base + o_act);
+        rb->wtab = (float*)(base + o_wtab);
+    }
+    return cv.off;
+}
+}  // namespace
+
+moe_status moe_route_static(const void* x, int32_t T, int32_t hidden, int32_t n_experts, int32_t top_k,
+                            const void* router_w, const float* router_bias, int32_t* ids, float* w, int32_t* offsets,
+                            int32_t* perm, void* hip_stream) {
+    if (T < 0 || T > kMaxDecodeT) return fail(MOE_ERANGE, "T %d outside [0, %d]", T, kMaxDecodeT);
+    if (hidden <= 0 || hidden % 32 || hidden > 4096)
+        return fail(MOE_EINVAL, "hidden %d must be a positive multiple of 32, at most 4096", hidden);
+    if (n_experts < 1 || n_experts > kMaxExperts)
+        return fail(MOE_EINVAL, "n_experts %d outside [1, %d]", n_experts, kMaxExperts);
+    if (top_k < 1 || top_k > std::min(n_experts, kMaxTopK))
+        return fail(MOE_EINVAL, "top_k %d outside [1, min(E, %d)]", top_k, kMaxTopK);
+    const size_t need = carve_static_route(nullptr, n_experts, top_k, hidden, nullptr);
+    if (need > kStaticScratchBytes)
+        return fail(MOE_ERANGE, "routing scratch of %zu bytes exceeds the static %zu bytes", need,
+                    kStaticScratchBytes);
+    if (T == 0) return MOE_OK;
+    if (!x || !router_w || !ids || !w) return fail(MOE_EINVAL, "x, router_w, ids and w are required");
+    if (!aligned16(x) || !aligned16(router_w)) return fail(MOE_EINVAL, "x and router_w must be 16-byte aligned");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MOE_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kStaticMaxDevices) return fail(MOE_EINVAL, "device %d above the supported %d", dev,
+                                                         kStaticMaxDevices);
+    uint8_t* base = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_static_mu);
+        if (!g_static_ptr[dev]) {
+            void* p = nullptr;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p) return fail(MOE_EHIP, "hipGetSymbolAddress: %s", hipGetErrorString(e));
+            g_static_ptr[dev] = p;
+        }
+        base = (uint8_t*)g_static_ptr[dev];
+    }
+    RouteBufs rb{};
+    carve_static_route(base, n_experts, top_k, hidden, &rb);
+    // results go straight to the caller's buffers where given
+    rb.ids = ids;
+    rb.w = w;
+    if (offsets) rb.offsets = offsets;
+    if (perm) rb.perm = perm;
+    const Geom g = make_geom(hidden, 32, n_experts, 0, top_k, MOE_Q4B32, 1);
+    const Launch lc{(hipStream_t)hip_stream};
+    e = launch_router_decode((const uint16_t*)x, T, (const uint16_t*)router_w, router_bias, g, rb, nullptr, lc);
+    if (e != hipSuccess) return fail(MOE_EHIP, "router kernel launch: %s", hipGetErrorString(e));
+    e = launch_topk_sort_decode(T, g, rb, nullptr, nullptr, 0, nullptr, nullptr, lc);
+    if (e != hipSuccess) return fail(MOE_EHIP, "top-k kernel launch: %s", hipGetErrorString(e));
     return MOE_OK;
 }
 

@@ -92,3 +92,21 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_static_route_argument_checks():
+    """moe_route_static validates before touching any device: window, geometry and top-k limits."""
+    import quantized_expert_ffn_softmax_amd as moe
+    lib = moe.lib()
+    f = lib.moe_route_static
+    assert f(None, 9, 256, 16, 2, None, None, None, None, None, None, None) == moe.MOE_ERANGE
+    assert f(None, -1, 256, 16, 2, None, None, None, None, None, None, None) == moe.MOE_ERANGE
+    assert f(None, 4, 100, 16, 2, None, None, None, None, None, None, None) == moe.MOE_EINVAL
+    assert f(None, 4, 8192, 16, 2, None, None, None, None, None, None, None) == moe.MOE_EINVAL
+    assert f(None, 4, 256, 0, 1, None, None, None, None, None, None, None) == moe.MOE_EINVAL
+    assert f(None, 4, 256, 2000, 2, None, None, None, None, None, None, None) == moe.MOE_EINVAL
+    assert f(None, 4, 256, 16, 17, None, None, None, None, None, None, None) == moe.MOE_EINVAL
+    assert f(None, 4, 256, 8, 9, None, None, None, None, None, None, None) == moe.MOE_EINVAL
+    assert f(None, 4, 256, 16, 2, None, None, None, None, None, None, None) == moe.MOE_EINVAL  # NULL pointers
+    assert b"required" in lib.moe_last_error()
+    assert f(None, 0, 4096, 1024, 16, None, None, None, None, None, None, None) == moe.MOE_OK  # T = 0: no-op
