@@ -21,12 +21,14 @@ and the roofline is that of the gate/up grouped GEMM on bf16 MFMA.
 C2_q2b64 and C3_q2b64 are C2 and C3 with q2b64 experts (one fp16 scale per
 64 2-bit codes: 2.25 bits per weight, 1,382,400 bytes per expert).
 
-Decode: the timed steps replay a HIP graph, of one input cycle when the step
-count is a multiple of it and of exactly the timed steps otherwise; the eager
-time of the same steps is reported as ms_per_step_eager.  After the timed
-region, the spread of the step time (ms_per_step_p10_p50_p90) comes from
-further replays of the same graph, each timed on its own (per step), or, for
-the prefill chunk, from every chunk between events of its own.
+Single decode layers (C2): the timed steps replay a HIP graph captured here, of
+one input cycle when the step count is a multiple of it and of exactly the
+timed steps otherwise; the eager time of the same steps is reported as
+ms_per_step_eager, and the spread (ms_per_step_p10_p50_p90) comes from further
+replays, each timed on its own.  Chains (C3, C4): each step is one
+moe_forward call, which replays the library's own HIP graph of the chain; the
+spread comes from every step between events of its own, as for the prefill
+chunk.
 
 Printed: one JSON line with tokens/s, HBM GB/s on expert bytes, the roofline
 of the dominant kernel (gate/up, measured with HIP events recorded around
@@ -138,39 +140,56 @@ def main():
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1)
 
-    ms_eager = timed_eager()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        graph.capture_begin()
-        for i in range(gsteps):
+    if chain:
+        # a chain step is one moe_forward of every layer: the library replays its own HIP graph of the
+        # whole chain (captured on the first call with these buffers), nothing is captured here
+        for i in range(len(xs)):
             step(i)
-        graph.capture_end()
-    torch.cuda.current_stream().wait_stream(side)
-    graph.replay()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(replays):
+        torch.cuda.synchronize()
+        ms_total = timed_eager()
+        ms_eager = ms_total
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        evs[0].record()
+        for i in range(args.steps):
+            step(i)
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        spread = np.percentile([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)], [10, 50, 90])
+        launch_desc = f"one moe_forward per step, replaying the library's HIP graph of the {L}-layer chain"
+    else:
+        ms_eager = timed_eager()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            graph.capture_begin()
+            for i in range(gsteps):
+                step(i)
+            graph.capture_end()
+        torch.cuda.current_stream().wait_stream(side)
         graph.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    ms_total = ev0.elapsed_time(ev1)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(replays):
+            graph.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        ms_total = ev0.elapsed_time(ev1)
+        # spread: further replays of the same graph, each timed on its own, per step
+        n_rep = max(5, replays)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep + 1)]
+        evs[0].record()
+        for r in range(n_rep):
+            graph.replay()
+            evs[r + 1].record()
+        torch.cuda.synchronize()
+        spread = np.percentile([evs[r].elapsed_time(evs[r + 1]) / gsteps for r in range(n_rep)], [10, 50, 90])
+        launch_desc = f"{replays} replay(s) of a HIP graph of {gsteps} steps (captured by the caller)"
     ms_per_step = ms_total / args.steps
-
-    # spread: further replays of the same graph, each timed on its own, per step
-    n_rep = max(5, replays)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep + 1)]
-    evs[0].record()
-    for r in range(n_rep):
-        graph.replay()
-        evs[r + 1].record()
-    torch.cuda.synchronize()
-    spread = np.percentile([evs[r].elapsed_time(evs[r + 1]) / gsteps for r in range(n_rep)], [10, 50, 90])
     tokens_per_s = T * args.steps / (ms_total / 1e3)
-    log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step as {replays} replay(s) of a "
-        f"{gsteps}-step HIP graph, {ms_eager / args.steps * 1e3:.1f} us/step eager")
+    log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step ({launch_desc}), "
+        f"{ms_eager / args.steps * 1e3:.1f} us/step eager")
 
     # ---- routing of every (layer, window) pair used: distinct experts -> algorithmic bytes
     n_pairs = L if chain else int(np.lcm(L, len(xs)))
@@ -260,7 +279,7 @@ def main():
                                                   f"{L}-layer MoE-only decode chain with residual per step")),
             "T": T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "S": cfg.S, "k": cfg.k, "layers_resident": L,
             "quant": {1: "q4b32", 2: "q2b32", 3: "q2b64"}[cfg.fmt], "seed": args.seed,
-            "launch": f"{replays} replay(s) of a HIP graph of {gsteps} steps (captured by the caller)",
+            "launch": launch_desc,
         },
         "hbm_GBps": round(hbm_gbps, 1),
         "hbm_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),

@@ -78,6 +78,16 @@ struct moe_ctx {
     // profiling: event pairs around kernel launches
     std::vector<hipEvent_t> prof_events;
     std::vector<moe_kernel_time> prof_recs;
+    // whole decode chains as HIP graphs, one per (layer range, T, flags, buffers), least recently used evicted
+    struct ChainGraph {
+        int32_t layer_begin, layer_count, T, flags;
+        const void *x, *y, *trace_x, *trace_ids, *trace_w, *token_ids;
+        hipGraphExec_t exec;
+        uint64_t used;
+    };
+    std::vector<ChainGraph> graphs;
+    uint64_t graph_clock = 0;
+    hipStream_t capture_stream = nullptr;
 };
 
 namespace {
@@ -93,8 +103,15 @@ moe_status hip_fail(moe_ctx* c, hipError_t e, const char* what) {
         if (e_ != hipSuccess) return hip_fail(ctx, e_, #call); \
     } while (0)
 
+void drop_graphs(moe_ctx* c) {
+    for (auto& gr : c->graphs) hipGraphExecDestroy(gr.exec);
+    c->graphs.clear();
+}
+
 void free_ctx(moe_ctx* c) {
     if (!c) return;
+    drop_graphs(c);
+    if (c->capture_stream) hipStreamDestroy(c->capture_stream);
     for (hipEvent_t e : c->prof_events) hipEventDestroy(e);
     if (c->load_stream) hipStreamSynchronize(c->load_stream);
     for (int i = 0; i < 2; ++i) {
@@ -287,8 +304,9 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
         free_ctx(c);
         return fail(MOE_EHIP, "scratch initialisation failed");
     }
-    // bounded staging for uploads
-    if (hipStreamCreateWithFlags(&c->load_stream, hipStreamNonBlocking) != hipSuccess) {
+    // bounded staging for uploads; a stream of its own for capturing decode chains
+    if (hipStreamCreateWithFlags(&c->load_stream, hipStreamNonBlocking) != hipSuccess ||
+        hipStreamCreateWithFlags(&c->capture_stream, hipStreamNonBlocking) != hipSuccess) {
         free_ctx(c);
         return fail(MOE_EHIP, "stream creation failed");
     }
@@ -343,6 +361,8 @@ moe_status moe_load_experts(moe_ctx* c, const moe_layer_weights* w) {
         }
     }
     HIP_TRY(c, hipSetDevice(c->cfg.device));
+    // captured chains hold the hash tables' addresses: an upload may move them
+    drop_graphs(c);
     if (w->tid2eid) {
         const size_t tb = (size_t)w->vocab * g.k * 4;
         if (c->tid2eid[w->layer] && c->vocab[w->layer] != w->vocab) {
@@ -513,6 +533,13 @@ moe_status moe_route(moe_ctx* c, int32_t layer, const void* x, int32_t T, const 
     return MOE_OK;
 }
 
+}  // extern "C"
+namespace {
+moe_status forward_layers(moe_ctx* c, const moe_fwd_args* a, hipStream_t st);
+moe_status forward_graph(moe_ctx* c, const moe_fwd_args* a, hipStream_t st);
+}  // namespace
+extern "C" {
+
 moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
     if (!c || !a) return fail(MOE_EINVAL, "ctx or args is NULL");
     if (c->poisoned) return fail(MOE_ESTATE, "context is poisoned by an earlier HIP failure");
@@ -534,10 +561,66 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
         if (c->tid2eid[l] && (!a->token_ids || ((uintptr_t)a->token_ids & 3u)))
             return fail(MOE_EINVAL, "layer %d is hash-routed: token_ids (4-byte aligned) is required", l);
     }
-    const int T = a->T;
-    const bool pf = T > kMaxDecodeT;
     hipStream_t st = (hipStream_t)hip_stream;
     HIP_TRY(c, hipSetDevice(c->cfg.device));
+    // A decode chain (several layers of a window) replays a HIP graph of the whole chain, captured once per
+    // (layers, T, flags, buffers); profiled calls and calls made while the caller's stream is being captured
+    // (the caller's graph then records the kernels) run eagerly.
+    if (a->T <= kMaxDecodeT && a->layer_count > 1 && !(a->flags & MOE_FWD_PROFILE)) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        HIP_TRY(c, hipStreamIsCapturing(st, &cs));
+        if (cs == hipStreamCaptureStatusNone) return forward_graph(c, a, st);
+    }
+    return forward_layers(c, a, st);
+}
+
+}  // extern "C"
+
+namespace {
+
+moe_status forward_graph(moe_ctx* c, const moe_fwd_args* a, hipStream_t st) {
+    const void* key[6] = {a->x, a->y, a->trace_x, a->trace_ids, a->trace_w, a->token_ids};
+    moe_ctx::ChainGraph* hit = nullptr;
+    for (auto& gr : c->graphs)
+        if (gr.layer_begin == a->layer_begin && gr.layer_count == a->layer_count && gr.T == a->T &&
+            gr.flags == a->flags && gr.x == key[0] && gr.y == key[1] && gr.trace_x == key[2] && gr.trace_ids == key[3] &&
+            gr.trace_w == key[4] && gr.token_ids == key[5])
+            hit = &gr;
+    if (!hit) {
+        constexpr size_t kMaxGraphs = 32;
+        if (c->graphs.size() >= kMaxGraphs) {
+            auto lru = std::min_element(c->graphs.begin(), c->graphs.end(),
+                                        [](const moe_ctx::ChainGraph& p, const moe_ctx::ChainGraph& q) { return p.used < q.used; });
+            HIP_TRY(c, hipGraphExecDestroy(lru->exec));
+            c->graphs.erase(lru);
+        }
+        HIP_TRY(c, hipStreamBeginCapture(c->capture_stream, hipStreamCaptureModeThreadLocal));
+        const moe_status s = forward_layers(c, a, c->capture_stream);
+        hipGraph_t graph = nullptr;
+        const hipError_t e = hipStreamEndCapture(c->capture_stream, &graph);
+        if (s != MOE_OK) {
+            if (graph) hipGraphDestroy(graph);
+            return s;
+        }
+        if (e != hipSuccess) return hip_fail(c, e, "hipStreamEndCapture");
+        hipGraphExec_t exec = nullptr;
+        const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+        hipGraphDestroy(graph);
+        if (ei != hipSuccess) return hip_fail(c, ei, "hipGraphInstantiate");
+        c->graphs.push_back(moe_ctx::ChainGraph{a->layer_begin, a->layer_count, a->T, a->flags, key[0], key[1], key[2],
+                                                key[3], key[4], key[5], exec, 0});
+        hit = &c->graphs.back();
+    }
+    hit->used = ++c->graph_clock;
+    HIP_TRY(c, hipGraphLaunch(hit->exec, st));
+    return MOE_OK;
+}
+
+// The layers of one moe_forward call, launched on st (validated arguments).
+moe_status forward_layers(moe_ctx* c, const moe_fwd_args* a, hipStream_t st) {
+    const Geom& g = c->g;
+    const int T = a->T;
+    const bool pf = T > kMaxDecodeT;
     const int ES = g.E + g.S;
     const size_t xbytes = (size_t)T * g.H * 2;
     const uint16_t* xin = (const uint16_t*)a->x;
@@ -602,6 +685,10 @@ moe_status moe_forward(moe_ctx* c, const moe_fwd_args* a, void* hip_stream) {
     }
     return MOE_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 // ---------------------------------------------------------------- routing without allocation
 // moe_route_static: the decode-window routing kernels of moe_route (router
