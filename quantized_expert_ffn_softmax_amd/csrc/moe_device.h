@@ -108,6 +108,25 @@ template <int FMT> __device__ __forceinline__ u32x2_t load_scales(const uint8_t*
     else
         return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(chunk + 64 * QF<FMT>::kCW + n * 8));
 }
+// One interleaved G|U unit of q2 / q2b64 (chunk c of a row tile of both):
+// lane's codes of G and U in one 16-byte load, row n's scales of both in one
+// load (16 bytes for q2, 8 for q2b64).
+template <int FMT>
+__device__ __forceinline__ void load_gu_unit(const uint8_t* unit, int lane, int n, uint32_t* cg, uint32_t* cu,
+                                             u32x2_t& sg, u32x2_t& su) {
+    static_assert(FMT != 1, "q4 keeps G and U as separate matrices");
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(unit + lane * 16));
+    cg[0] = v.x; cg[1] = v.y; cu[0] = v.z; cu[1] = v.w;
+    if constexpr (FMT == 3) {
+        const u32x2_t sv = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(unit + 64 * 16 + n * 8));
+        sg = u32x2_t{sv.x, 0u};
+        su = u32x2_t{sv.y, 0u};
+    } else {
+        const u32x4_t sv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(unit + 64 * 16 + n * 16));
+        sg = u32x2_t{sv.x, sv.y};
+        su = u32x2_t{sv.z, sv.w};
+    }
+}
 template <int FMT> __device__ __forceinline__ float scale_of(u32x2_t s, int j) {
     if constexpr (FMT == 3) return h2f((j & 2) ? (s.x >> 16) : (s.x & 0xFFFFu));
     const uint32_t w = (j & 2) ? s.y : s.x;

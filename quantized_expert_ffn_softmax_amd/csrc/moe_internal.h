@@ -26,8 +26,13 @@
 // exact MFMA operand with one shift and one and-or; the offset 128 + o is
 // removed after the contraction with the per-block sums of the other operand.
 //
-// An expert slot holds G (F/16 row tiles, K = H), then U (same), then D
-// (H/16 row tiles, K = F), and is padded to a multiple of 256 bytes.
+// An expert slot holds G and U (F/16 row tiles each, K = H), then D (H/16 row
+// tiles, K = F), and is padded to a multiple of 256 bytes.  q4: G, then U, as
+// two matrices.  q2 and q2b64: G and U interleaved chunk by chunk, so that a
+// lane of the decode gate/up kernel reads both with one 16-byte load: unit
+// (rt, c) at (rt nch + c) 2 chunk_bytes holds 64 lanes x 16 bytes (the lane's
+// G code bytes, then its U code bytes), then 16 rows x 2 s bytes (row n's G
+// scales, then its U scales; s = 8 for q2, 4 for q2b64).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -55,7 +60,7 @@ struct Geom {
     int H, F, E, S, k, fmt, L;
     MatGeom gu;      // G and U: [F x H]
     MatGeom dn;      // D: [H x F]
-    int64_t g_off, u_off, d_off;
+    int64_t g_off, u_off, d_off;  // g_off = u_off = 0 when G and U are interleaved (q2, q2b64)
     int64_t slot_bytes;
     int64_t canon_expert_bytes;
 };
@@ -64,6 +69,7 @@ inline int code_bytes_per_lane(int fmt) { return fmt == 1 ? 16 : 8; }
 inline int scale_bytes_per_row(int fmt) { return fmt == 3 ? 4 : 8; }  // per chunk
 inline int canon_block_weights(int fmt) { return fmt == 3 ? 64 : 32; }
 inline int canon_block_bytes(int fmt) { return fmt == 2 ? 10 : 18; }
+inline bool gu_interleaved(int fmt) { return fmt != 1; }
 
 inline MatGeom make_mat(int rows, int K, int fmt) {
     MatGeom m;
@@ -83,7 +89,7 @@ inline Geom make_geom(int H, int F, int E, int S, int k, int fmt, int L) {
     g.gu = make_mat(F, H, fmt);
     g.dn = make_mat(H, F, fmt);
     g.g_off = 0;
-    g.u_off = g.gu.bytes;
+    g.u_off = gu_interleaved(fmt) ? 0 : g.gu.bytes;
     g.d_off = 2 * g.gu.bytes;
     g.slot_bytes = (2 * g.gu.bytes + g.dn.bytes + 255) / 256 * 256;
     g.canon_expert_bytes = 3LL * H * F / canon_block_weights(fmt) * canon_block_bytes(fmt);

@@ -87,8 +87,18 @@ __global__ __launch_bounds__(256) void k_repack(const uint8_t* __restrict__ cano
     const int bsh = g.fmt == 3 ? 1 : 0;               // log2(canonical block weights / 32)
     const int64_t gu_bytes = (int64_t)g.F * (g.H / 32 >> bsh) * bb;
     const uint8_t* src = canon + (int64_t)ex * g.canon_expert_bytes + (mat == 0 ? 0 : mat == 1 ? gu_bytes : 2 * gu_bytes);
-    uint8_t* dst = slots + (int64_t)ex * g.slot_bytes + (mat == 0 ? g.g_off : mat == 1 ? g.u_off : g.d_off) +
-                   (int64_t)rt * m.tile_bytes + (int64_t)c * m.chunk_bytes;
+    // lane stride of the codes, scale-row stride, and this matrix's byte inside both
+    // (G and U of q2 / q2b64 share interleaved units of two chunks' size)
+    const bool il = mat < 2 && g.fmt != 1;
+    const int cwb = g.fmt == 1 ? 16 : 8, sb = g.fmt == 3 ? 4 : 8;
+    uint8_t* dst = slots + (int64_t)ex * g.slot_bytes;
+    if (il)
+        dst += ((int64_t)rt * m.nch + c) * 2 * m.chunk_bytes;
+    else
+        dst += (mat == 0 ? g.g_off : mat == 1 ? g.u_off : g.d_off) + (int64_t)rt * m.tile_bytes +
+               (int64_t)c * m.chunk_bytes;
+    const int lstride = il ? 2 * cwb : cwb, sstride = il ? 2 * sb : sb;
+    const int lpos = il ? mat * cwb : 0, spos = il ? mat * sb : 0;
     const int n = lane & 15, gs = lane >> 4;
     const int row = rt * 16 + n;
     const int o = g.fmt == 1 ? 8 : 2;
@@ -107,7 +117,7 @@ __global__ __launch_bounds__(256) void k_repack(const uint8_t* __restrict__ cano
                 v |= (code(b, 8 * gs + 2 * p) << (4 * p)) | (code(b, 8 * gs + 2 * p + 1) << (16 + 4 * p));
             w[j] = v;
         }
-        *reinterpret_cast<u32x4_t*>(dst + lane * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4_t*>(dst + lane * lstride + lpos) = u32x4_t{w[0], w[1], w[2], w[3]};
     } else {
         uint32_t w[2];
         for (int jj = 0; jj < 2; ++jj) {
@@ -119,7 +129,7 @@ __global__ __launch_bounds__(256) void k_repack(const uint8_t* __restrict__ cano
             }
             w[jj] = v;
         }
-        *reinterpret_cast<u32x2_t*>(dst + lane * 8) = u32x2_t{w[0], w[1]};
+        *reinterpret_cast<u32x2_t*>(dst + lane * lstride + lpos) = u32x2_t{w[0], w[1]};
     }
     if (gs == 0) {
         // scales of the chunk's canonical blocks (4, or 2 for q2b64); padding blocks get 0
@@ -134,11 +144,11 @@ __global__ __launch_bounds__(256) void k_repack(const uint8_t* __restrict__ cano
                 s[j] = 0;
             }
         }
-        uint8_t* sdst = dst + 64 * (g.fmt == 1 ? 16 : 8);
+        uint8_t* sdst = dst + 64 * lstride + n * sstride + spos;
         if (g.fmt == 3)
-            *reinterpret_cast<uint32_t*>(sdst + n * 4) = (uint32_t)s[0] | ((uint32_t)s[1] << 16);
+            *reinterpret_cast<uint32_t*>(sdst) = (uint32_t)s[0] | ((uint32_t)s[1] << 16);
         else
-            *reinterpret_cast<u32x2_t*>(sdst + n * 8) =
+            *reinterpret_cast<u32x2_t*>(sdst) =
                 u32x2_t{(uint32_t)s[0] | ((uint32_t)s[1] << 16), (uint32_t)s[2] | ((uint32_t)s[3] << 16)};
     }
 }
@@ -507,7 +517,8 @@ __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restric
     const MatGeom& mg = g.gu;
     const int c0 = wave * mg.nch / 4, c1 = (wave + 1) * mg.nch / 4;
     constexpr int CWN = FMT == 1 ? 4 : 2;
-    const int64_t base = (int64_t)e * g.slot_bytes + (int64_t)rt * mg.tile_bytes;
+    // q4: row tile rt of G and of U; q2 / q2b64: the interleaved G|U units of row tile rt
+    const int64_t base = (int64_t)e * g.slot_bytes + (int64_t)rt * mg.tile_bytes * (FMT == 1 ? 1 : 2);
     const uint8_t* Gt = slots + base + g.g_off;
     const uint8_t* Ut = slots + base + g.u_off;
     const int h8 = g.H / 8, xs8 = h8 + 1;
@@ -529,11 +540,15 @@ __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restric
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
         const int c = min(c0 + j, mg.nch - 1);
-        const int64_t off = (int64_t)c * mg.chunk_bytes;
-        load_codes<FMT>(Gt + off, lane, cg[j]);
-        sg[j] = load_scales<FMT>(Gt + off, n);
-        load_codes<FMT>(Ut + off, lane, cu[j]);
-        su[j] = load_scales<FMT>(Ut + off, n);
+        if constexpr (FMT == 1) {
+            const int64_t off = (int64_t)c * mg.chunk_bytes;
+            load_codes<FMT>(Gt + off, lane, cg[j]);
+            sg[j] = load_scales<FMT>(Gt + off, n);
+            load_codes<FMT>(Ut + off, lane, cu[j]);
+            su[j] = load_scales<FMT>(Ut + off, n);
+        } else {
+            load_gu_unit<FMT>(Gt + (int64_t)c * 2 * mg.chunk_bytes, lane, n, cg[j], cu[j], sg[j], su[j]);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
     // routing weights of this lane's tokens R gs + i (used by wave 0 in the epilogue)

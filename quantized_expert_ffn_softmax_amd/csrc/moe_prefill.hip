@@ -566,17 +566,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // Codes of one chunk: soff = the chunk's byte offset in the expert slot;
 // offc / offs = the lane's byte offsets of its first code word and of its
-// scales in a chunk.  A row tile past the matrix (N not a multiple of the
-// tile) reads the last one again: the columns it feeds are never stored.
+// scales in a chunk; lstr = the byte stride of the slot's code lanes (16 for
+// q4, and for the interleaved G|U units of q2 / q2b64; 8 for their D).  A row
+// tile past the matrix (N not a multiple of the tile) reads the last one
+// again: the columns it feeds are never stored.
 template <int FMT>
 __device__ __forceinline__ void load_bcodes(BCodes<FMT>& b, __amdgpu_buffer_rsrc_t r, uint32_t soff, uint32_t offc,
-                                            uint32_t offs) {
+                                            uint32_t offs, uint32_t lstr) {
     if constexpr (FMT == 1) {
         b.c0 = __builtin_amdgcn_raw_buffer_load_b128(r, offc, soff, 0);
         b.c1 = __builtin_amdgcn_raw_buffer_load_b128(r, offc + 32 * 16, soff, 0);
     } else {
         b.c0 = __builtin_amdgcn_raw_buffer_load_b64(r, offc, soff, 0);
-        b.c1 = __builtin_amdgcn_raw_buffer_load_b64(r, offc + 32 * 8, soff, 0);
+        b.c1 = __builtin_amdgcn_raw_buffer_load_b64(r, offc + 32 * lstr, soff, 0);
     }
     if constexpr (FMT == 3)
         b.sc = u32x2_t{__builtin_amdgcn_raw_buffer_load_b32(r, offs, soff, 0), 0u};
@@ -655,7 +657,8 @@ struct GemmItem {
     uint32_t boffc[2];          // per 32-column group: byte offset of this lane's code words in chunk 0
     uint32_t boffs[2];          // ... and of its row's scales
     int row0, nrows, nt, wave, nk, K;
-    uint32_t chunk_bytes;
+    uint32_t chunk_bytes;       // byte stride of consecutive chunks of a row tile
+    uint32_t lstr;              // byte stride of the code lanes of a chunk
 };
 
 // Main loop and epilogue for NS 32-row slices.  Every slice of the item holds
@@ -703,7 +706,7 @@ __device__ __forceinline__ void gemm_item(GemmItem& it, uint8_t* As, const Geom&
     BCodes<FMT> bc0[2], bc1[2];
     load_a(0, 0);
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) load_bcodes<FMT>(bc0[gi], it.br, 0u, it.boffc[gi], it.boffs[gi]);
+    for (int gi = 0; gi < 2; ++gi) load_bcodes<FMT>(bc0[gi], it.br, 0u, it.boffc[gi], it.boffs[gi], it.lstr);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
     __syncthreads();
     // LDS byte offset of this lane's fragment row (slice 0) and its segment swizzle
@@ -718,7 +721,7 @@ __device__ __forceinline__ void gemm_item(GemmItem& it, uint8_t* As, const Geom&
         load_a(kn, buf ^ 1);
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi)
-            load_bcodes<FMT>(nb[gi], it.br, (uint32_t)kn * it.chunk_bytes, it.boffc[gi], it.boffs[gi]);
+            load_bcodes<FMT>(nb[gi], it.br, (uint32_t)kn * it.chunk_bytes, it.boffc[gi], it.boffs[gi], it.lstr);
         // the next chunk is requested before this chunk's work (the scheduler
         // would otherwise sink the loads to their use)
         __builtin_amdgcn_sched_barrier(0);
@@ -839,7 +842,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     it.K = MODE == 1 ? g.H : g.F;
     const MatGeom& mg = MODE == 1 ? g.gu : g.dn;
     it.nk = mg.nch;
-    it.chunk_bytes = (uint32_t)mg.chunk_bytes;
+    // G and U of q2 / q2b64 come in interleaved units of two chunks' size
+    constexpr bool il = MODE == 1 && FMT != 1;
+    it.chunk_bytes = (uint32_t)mg.chunk_bytes * (il ? 2u : 1u);
+    it.lstr = il ? 16u : (uint32_t)QF<FMT>::kCW;
     it.br = make_rsrc(slots + (int64_t)grp * g.slot_bytes, (uint32_t)g.slot_bytes);
     const int n = lane & 31, half = lane >> 5;
 #pragma unroll
@@ -853,10 +859,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             rt = nt * 16 + 4 * it.wave + 2 * gi + (n >> 4);
             base = (uint32_t)g.d_off;
         }
-        // lane l takes the slot-lanes (n % 16, half) and (n % 16, half + 2) of its row tile
-        const uint32_t tile = base + (uint32_t)min(rt, mg.rows / 16 - 1) * (uint32_t)mg.tile_bytes;
-        it.boffc[gi] = tile + (uint32_t)((n & 15) + 16 * half) * QF<FMT>::kCW;
-        it.boffs[gi] = tile + 64 * QF<FMT>::kCW + (uint32_t)(n & 15) * (FMT == 3 ? 4 : 8);
+        // lane l takes the slot-lanes (n % 16, half) and (n % 16, half + 2) of its row tile;
+        // interleaved G|U units: G's bytes first in every lane entry and scale row, then U's
+        constexpr uint32_t sb = FMT == 3 ? 4 : 8;
+        const uint32_t rtc = (uint32_t)min(rt, mg.rows / 16 - 1);
+        const uint32_t tile = base + rtc * (uint32_t)mg.nch * it.chunk_bytes;
+        const uint32_t part = il ? (uint32_t)gi : 0u;
+        it.boffc[gi] = tile + (uint32_t)((n & 15) + 16 * half) * it.lstr + part * QF<FMT>::kCW;
+        it.boffs[gi] = tile + 64 * it.lstr + (uint32_t)(n & 15) * sb * (il ? 2u : 1u) + part * sb;
     }
     // A: lane l of instruction q of wave w fetches segment (l % 16) ^ (r % 16)
     // of tile row r = 32 w + 4 q + l / 16
