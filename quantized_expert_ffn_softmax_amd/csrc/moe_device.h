@@ -108,13 +108,14 @@ template <int FMT> __device__ __forceinline__ u32x2_t load_scales(const uint8_t*
     else
         return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(chunk + 64 * QF<FMT>::kCW + n * 8));
 }
-// One interleaved G|U unit of q2 / q2b64 (chunk c of a row tile of both):
-// lane's codes of G and U in one 16-byte load, row n's scales of both in one
-// load (16 bytes for q2, 8 for q2b64).
+// One interleaved unit of q2 / q2b64 (chunk c of two row tiles stored
+// together: of G and U, or of D's row tiles 2 rp and 2 rp + 1): the lane's
+// codes of both in one 16-byte load, row n's scales of both in one load (16
+// bytes for q2, 8 for q2b64).
 template <int FMT>
-__device__ __forceinline__ void load_gu_unit(const uint8_t* unit, int lane, int n, uint32_t* cg, uint32_t* cu,
-                                             u32x2_t& sg, u32x2_t& su) {
-    static_assert(FMT != 1, "q4 keeps G and U as separate matrices");
+__device__ __forceinline__ void load_pair_unit(const uint8_t* unit, int lane, int n, uint32_t* cg, uint32_t* cu,
+                                               u32x2_t& sg, u32x2_t& su) {
+    static_assert(FMT != 1, "q4 slots are not interleaved");
     const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(unit + lane * 16));
     cg[0] = v.x; cg[1] = v.y; cu[0] = v.z; cu[1] = v.w;
     if constexpr (FMT == 3) {

@@ -32,7 +32,10 @@
 // lane of the decode gate/up kernel reads both with one 16-byte load: unit
 // (rt, c) at (rt nch + c) 2 chunk_bytes holds 64 lanes x 16 bytes (the lane's
 // G code bytes, then its U code bytes), then 16 rows x 2 s bytes (row n's G
-// scales, then its U scales; s = 8 for q2, 4 for q2b64).
+// scales, then its U scales; s = 8 for q2, 4 for q2b64).  Their D pairs its
+// row tiles the same way: unit (rp, c) at d_off + (rp nch + c) 2 chunk_bytes
+// holds row tiles 2 rp (first half of every lane entry and scale row) and
+// 2 rp + 1 (second half); H is a multiple of 32, so every tile has its pair.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>

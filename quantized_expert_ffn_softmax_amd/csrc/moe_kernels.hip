@@ -88,17 +88,18 @@ __global__ __launch_bounds__(256) void k_repack(const uint8_t* __restrict__ cano
     const int64_t gu_bytes = (int64_t)g.F * (g.H / 32 >> bsh) * bb;
     const uint8_t* src = canon + (int64_t)ex * g.canon_expert_bytes + (mat == 0 ? 0 : mat == 1 ? gu_bytes : 2 * gu_bytes);
     // lane stride of the codes, scale-row stride, and this matrix's byte inside both
-    // (G and U of q2 / q2b64 share interleaved units of two chunks' size)
-    const bool il = mat < 2 && g.fmt != 1;
+    // (q2 / q2b64 store G and U, and D's row tiles 2 rp, 2 rp + 1, in interleaved units of two chunks' size)
+    const bool il = g.fmt != 1;
     const int cwb = g.fmt == 1 ? 16 : 8, sb = g.fmt == 3 ? 4 : 8;
+    const int part = mat < 2 ? mat : rt & 1;  // which half of the unit
     uint8_t* dst = slots + (int64_t)ex * g.slot_bytes;
     if (il)
-        dst += ((int64_t)rt * m.nch + c) * 2 * m.chunk_bytes;
+        dst += (mat < 2 ? 0 : g.d_off) + ((int64_t)(mat < 2 ? rt : rt >> 1) * m.nch + c) * 2 * m.chunk_bytes;
     else
         dst += (mat == 0 ? g.g_off : mat == 1 ? g.u_off : g.d_off) + (int64_t)rt * m.tile_bytes +
                (int64_t)c * m.chunk_bytes;
     const int lstride = il ? 2 * cwb : cwb, sstride = il ? 2 * sb : sb;
-    const int lpos = il ? mat * cwb : 0, spos = il ? mat * sb : 0;
+    const int lpos = il ? part * cwb : 0, spos = il ? part * sb : 0;
     const int n = lane & 15, gs = lane >> 4;
     const int row = rt * 16 + n;
     const int o = g.fmt == 1 ? 8 : 2;
@@ -547,7 +548,7 @@ __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restric
             load_codes<FMT>(Ut + off, lane, cu[j]);
             su[j] = load_scales<FMT>(Ut + off, n);
         } else {
-            load_gu_unit<FMT>(Gt + (int64_t)c * 2 * mg.chunk_bytes, lane, n, cg[j], cu[j], sg[j], su[j]);
+            load_pair_unit<FMT>(Gt + (int64_t)c * 2 * mg.chunk_bytes, lane, n, cg[j], cu[j], sg[j], su[j]);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -690,21 +691,26 @@ hipError_t launch_gateup_decode(const uint16_t* x, int T, const uint8_t* layer_s
 // ---------------------------------------------------------------- down projection
 constexpr int kRing = 8;  // chunks in flight per wave beyond the one being multiplied
 
-// Grid (ceil(H/128), min(E, T k) + S), 512 threads.  Workgroup (rg, a)
+// Grid (ceil(H/128), min(E, T k) + S), 8 / RP waves.  Workgroup (rg, a)
 // computes the down projection of active expert a for rows 128rg..128rg+127
-// (wave w: row tile 8rg+w).  The workgroup first requests the expert's A
-// fragments (token t: v hi in row 4 (t % 4) + 2 (t / 4), v lo in the row
-// after, so a lane's result registers 0, 1 hold token lane / 16 and 2, 3 token
-// lane / 16 + 4; NV = 2 for T <= 4 skips the latter and stages the compact
-// 32-lane fragments: the lanes of the zero rows take a zero operand), then each wave requests the
-// first kRing chunks of its row tile; the fragments go to LDS as soon as they
-// arrive and every further chunk is requested as one is consumed.  K = F fits
-// one pass (nch <= NC).  Output: part[a][t][row].
-template <int FMT, int NC, int FPER, int NV>
-__global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots, Geom g,
-                                                     const int32_t* __restrict__ nact, const int32_t* __restrict__ act,
-                                                     int maxA, const uint32_t* __restrict__ afrag,
-                                                     const float* spart, float* __restrict__ part) {
+// (wave w: row tiles 8rg + RP w .. + RP - 1; RP = 2 for q2 / q2b64, whose D
+// stores row tiles in pairs, so one 16-byte load per lane brings the codes of
+// both and each operand fragment read from LDS feeds both).  The workgroup
+// first requests the expert's A fragments (token t: v hi in row 4 (t % 4) +
+// 2 (t / 4), v lo in the row after, so a lane's result registers 0, 1 hold
+// token lane / 16 and 2, 3 token lane / 16 + 4; NV = 2 for T <= 4 skips the
+// latter and stages the compact 32-lane fragments: the lanes of the zero rows
+// take a zero operand), then each wave requests the first kRing chunks of its
+// row tiles; the fragments go to LDS as soon as they arrive and every further
+// chunk is requested as one is consumed.  K = F fits one pass (nch <= NC).
+// Output: part[a][t][row].
+template <int FMT, int NC, int FPER, int NV, int RP>
+__global__ __launch_bounds__(512 / RP) void k_down_decode(int T, const uint8_t* slots, Geom g,
+                                                          const int32_t* __restrict__ nact,
+                                                          const int32_t* __restrict__ act, int maxA,
+                                                          const uint32_t* __restrict__ afrag, const float* spart,
+                                                          float* __restrict__ part) {
+    static_assert(RP == 1 || FMT != 1, "row-tile pairs exist for q2 / q2b64 only");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int a = blockIdx.y;
     const int na = nact[0];
@@ -715,8 +721,9 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots
     const int n = lane & 15, gs = lane >> 4, m = lane & 15;
     const MatGeom& md = g.dn;
     const int nbp = md.nch * 4;
-    const int rt = rg * 8 + wave;
+    const int rt = rg * 8 + wave * RP;  // first row tile of this wave
     const bool live = rt < g.H / 16;
+    // RP = 1: row tile rt; RP = 2: the unit row of tiles rt, rt + 1 (units of two chunks' size)
     const uint8_t* Dt = slots + (int64_t)e * g.slot_bytes + g.d_off + (int64_t)(live ? rt : 0) * md.tile_bytes;
     constexpr int CWN = FMT == 1 ? 4 : 2;
     constexpr int FL = NV == 2 ? 32 : 64;  // fragment lanes stored per block
@@ -728,24 +735,31 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots
     StageRegs<FPER> fst;
     fst.issue(reinterpret_cast<const u32x4_t*>(afrag) + (int64_t)a * nbp * FL, nbp * FL);
     const float* sp = spart + (int64_t)a * nbp * 32;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, corr = acc;
+    f32x4_t acc[RP], corr[RP];
+#pragma unroll
+    for (int r = 0; r < RP; ++r) acc[r] = corr[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // ring depth: kRing chunks; 2 for the 16-chunk case (F = 2048), which keeps
     // the kernel at 58 VGPRs, i.e. 8 waves per SIMD, so that a DeepSeek-shaped
     // call's whole grid is resident at once (measured faster than a ring of 4)
     constexpr int R = NC < kRing ? NC : (NC > 8 ? 2 : kRing);
-    uint32_t cw[R][CWN];
-    u32x2_t sc[R];
+    uint32_t cw[R][RP][CWN];
+    u32x2_t sc[R][RP];
     float s0[R], s1[R];
     // ring of R chunks (codes, scales and the block sums of the fragment rows)
     // with unconditional (clamped) loads, fully unrolled over NC
     auto load = [&](int c, int i) {
         const int cc = min(c, md.nch - 1);
-        const int64_t off = (int64_t)cc * md.chunk_bytes;
         const int bq = cc * 4 + gs;
         s0[i] = sp[bq * 32 + m];
         s1[i] = sp[bq * 32 + 16 + m];
-        load_codes<FMT>(Dt + off, lane, cw[i]);
-        sc[i] = load_scales<FMT>(Dt + off, n);
+        if constexpr (RP == 1) {
+            const int64_t off = (int64_t)cc * md.chunk_bytes;
+            load_codes<FMT>(Dt + off, lane, cw[i][0]);
+            sc[i][0] = load_scales<FMT>(Dt + off, n);
+        } else {
+            load_pair_unit<FMT>(Dt + (int64_t)cc * 2 * md.chunk_bytes, lane, n, cw[i][0], cw[i][1], sc[i][0],
+                                sc[i][1]);
+        }
     };
     // The fragments of all token rows are written (zeros for t >= T); chunks
     // past nch (NC > nch) carry zero scales and add nothing.
@@ -758,8 +772,11 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots
             const u32x4_t f = frag[min(c * 4 + j, nbp - 1) * FL + fl];
             A[j] = fzero || c * 4 + j >= md.nb ? u32x4_t{0u, 0u, 0u, 0u} : f;
         }
-        const u32x2_t scc = c < md.nch ? sc[i] : u32x2_t{0u, 0u};  // padding chunk (NC > nch): zero scales
-        chunk_mac<FMT, NV>(cw[i], scc, A, s0[i] + s1[i], gs, acc, corr);
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+            const u32x2_t scc = c < md.nch ? sc[i][r] : u32x2_t{0u, 0u};  // padding chunk (NC > nch): zero scales
+            chunk_mac<FMT, NV>(cw[i][r], scc, A, s0[i] + s1[i], gs, acc[r], corr[r]);
+        }
     };
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -785,24 +802,28 @@ __global__ __launch_bounds__(512) void k_down_decode(int T, const uint8_t* slots
         }
     }
     if (!live) return;
-    float v[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) v[i] = acc[i] - QF<FMT>::kBias * corr[i];
+    for (int r = 0; r < RP; ++r) {
+        float v[NV];
 #pragma unroll
-    for (int h = 0; h < NV / 2; ++h) {
-        const int t = gs + 4 * h;  // hi + lo
-        if (t < T) part[((int64_t)a * kMaxDecodeT + t) * g.H + rt * 16 + n] = v[2 * h] + v[2 * h + 1];
+        for (int i = 0; i < NV; ++i) v[i] = acc[r][i] - QF<FMT>::kBias * corr[r][i];
+#pragma unroll
+        for (int h = 0; h < NV / 2; ++h) {
+            const int t = gs + 4 * h;  // hi + lo
+            if (t < T) part[((int64_t)a * kMaxDecodeT + t) * g.H + (rt + r) * 16 + n] = v[2 * h] + v[2 * h + 1];
+        }
     }
 }
 
 template <int FMT, int NC, int FPER, int NV>
 hipError_t launch_down_v(int T, const uint8_t* slots, const Geom& g, RouteBufs rb, DecodeBufs db, dim3 grid, int lds,
                          int maxA, const Launch& lc) {
+    constexpr int RP = FMT == 1 ? 1 : 2;  // row tiles per wave
     static int granted = 64 * 1024;
-    hipError_t e = ensure_lds(k_down_decode<FMT, NC, FPER, NV>, lds, granted);
+    hipError_t e = ensure_lds(k_down_decode<FMT, NC, FPER, NV, RP>, lds, granted);
     if (e != hipSuccess) return e;
-    launch(k_down_decode<FMT, NC, FPER, NV>, grid, dim3(512), lds, lc, T, slots, g, rb.nact, rb.act, maxA, db.afrag,
-           db.spart, db.part);
+    launch(k_down_decode<FMT, NC, FPER, NV, RP>, grid, dim3(512 / RP), lds, lc, T, slots, g, rb.nact, rb.act, maxA,
+           db.afrag, db.spart, db.part);
     return hipGetLastError();
 }
 
@@ -816,9 +837,13 @@ hipError_t launch_down_f(int T, const uint8_t* slots, const Geom& g, RouteBufs r
 template <int FMT, int NC>
 hipError_t launch_down_nc(int T, const uint8_t* slots, const Geom& g, RouteBufs rb, DecodeBufs db, dim3 grid, int lds,
                           int maxA, const Launch& lc) {
-    const int per = (g.dn.nch * 4 * (T <= 4 ? 32 : 64) + 511) / 512;  // <= 8 (F <= 2048)
+    const int threads = FMT == 1 ? 512 : 256;  // 8 / RP waves
+    const int per = (g.dn.nch * 4 * (T <= 4 ? 32 : 64) + threads - 1) / threads;  // <= 16 (F <= 2048)
     if (per <= 2) return launch_down_f<FMT, NC, 2>(T, slots, g, rb, db, grid, lds, maxA, lc);
     if (per <= 4) return launch_down_f<FMT, NC, 4>(T, slots, g, rb, db, grid, lds, maxA, lc);
+    if constexpr (FMT != 1) {  // 256 threads stage up to 16 fragments each
+        if (per > 8) return launch_down_f<FMT, NC, 16>(T, slots, g, rb, db, grid, lds, maxA, lc);
+    }
     return launch_down_f<FMT, NC, 8>(T, slots, g, rb, db, grid, lds, maxA, lc);
 }
 

@@ -842,8 +842,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     it.K = MODE == 1 ? g.H : g.F;
     const MatGeom& mg = MODE == 1 ? g.gu : g.dn;
     it.nk = mg.nch;
-    // G and U of q2 / q2b64 come in interleaved units of two chunks' size
-    constexpr bool il = MODE == 1 && FMT != 1;
+    // q2 / q2b64 store G and U, and D's row tiles 2 rp, 2 rp + 1, in interleaved units of two chunks' size
+    constexpr bool il = FMT != 1;
     it.chunk_bytes = (uint32_t)mg.chunk_bytes * (il ? 2u : 1u);
     it.lstr = il ? 16u : (uint32_t)QF<FMT>::kCW;
     it.br = make_rsrc(slots + (int64_t)grp * g.slot_bytes, (uint32_t)g.slot_bytes);
@@ -860,11 +860,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             base = (uint32_t)g.d_off;
         }
         // lane l takes the slot-lanes (n % 16, half) and (n % 16, half + 2) of its row tile;
-        // interleaved G|U units: G's bytes first in every lane entry and scale row, then U's
+        // interleaved units: G's (D: the even tile's) bytes first in every lane entry and
+        // scale row, then U's (the odd tile's)
         constexpr uint32_t sb = FMT == 3 ? 4 : 8;
         const uint32_t rtc = (uint32_t)min(rt, mg.rows / 16 - 1);
-        const uint32_t tile = base + rtc * (uint32_t)mg.nch * it.chunk_bytes;
-        const uint32_t part = il ? (uint32_t)gi : 0u;
+        const uint32_t urow = il && MODE == 2 ? rtc >> 1 : rtc;  // unit row of the tile
+        const uint32_t tile = base + urow * (uint32_t)mg.nch * it.chunk_bytes;
+        const uint32_t part = !il ? 0u : MODE == 1 ? (uint32_t)gi : (rtc & 1u);
         it.boffc[gi] = tile + (uint32_t)((n & 15) + 16 * half) * it.lstr + part * QF<FMT>::kCW;
         it.boffs[gi] = tile + 64 * it.lstr + (uint32_t)(n & 15) * sb * (il ? 2u : 1u) + part * sb;
     }
