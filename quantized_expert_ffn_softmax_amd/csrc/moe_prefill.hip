@@ -247,15 +247,43 @@ __global__ __launch_bounds__(256) void k_pf_topk(const uint16_t* __restrict__ x,
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;  // no workgroup barrier below
+    // the fp32 logits' K-split partials (at most 8) are requested first, all at
+    // once (clamped split index, unconditional loads), then the x row
+    float pl[8][J];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            pl[q][j] = pb.logits[((int64_t)min(q, pb.ksplit - 1) * T + t) * E + min(lane + 64 * j, E - 1)];
     // x row in registers (H <= 4096: 8 x 16 bytes per lane; zero past H)
     const uint16_t* xr = x + (int64_t)t * H;
     u32x4_t xv[8];
-    double xx = 0.0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int h0 = lane * 8 + 512 * i;
-        xv[i] = u32x4_t{0u, 0u, 0u, 0u};
-        if (h0 < H) xv[i] = *reinterpret_cast<const u32x4_t*>(xr + h0);
+        xv[i] = *reinterpret_cast<const u32x4_t*>(xr + min(h0, H - 8));
+    }
+    // the bias values in one branch (its loads are waited for at the join, after the ones above)
+    float bv[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) bv[j] = 0.f;
+    if (bias) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) bv[j] = bias[min(lane + 64 * j, E - 1)];
+    }
+    float lf[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        // fp32 logit: the partials added in split order (a skipped partial keeps the sum), then the bias
+        float sl = pl[0][j];
+#pragma unroll
+        for (int q = 1; q < 8; ++q) sl = q < pb.ksplit ? sl + pl[q][j] : sl;
+        lf[j] = sl + bv[j];
+    }
+    double xx = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (lane * 8 + 512 * i >= H) xv[i] = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const double a = bf2f(xv[i][q] & 0xFFFFu), b = bf2f(xv[i][q] >> 16);
@@ -263,34 +291,40 @@ __global__ __launch_bounds__(256) void k_pf_topk(const uint16_t* __restrict__ x,
         }
     }
     const double xnorm = sqrt(wave_sum_f64(xx));
-    // k-th largest fp32 logit
-    float lf[J];
-    uint64_t key[J];
-    uint32_t taken = 0;
+    // k-th largest fp32 logit, on 32-bit keys: the order-preserving image of
+    // the logit with its low 10 bits replaced by 1023 - e (unique keys; each
+    // lane's J keys sorted once, then k rounds of the wave maximum of the
+    // lanes' heads).  Clearing 10 low bits never raises a key, so the value
+    // read back is at most the k-th largest logit: the threshold below can
+    // only admit more candidates.
+    uint32_t key[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int e = lane + 64 * j;
-        // fp32 logit: the router's K-split partials added in order, then the bias
-        const int ec = min(e, E - 1);
-        float sl = pb.logits[(int64_t)t * E + ec];
-        for (int q = 1; q < pb.ksplit; ++q) sl += pb.logits[((int64_t)q * T + t) * E + ec];
-        lf[j] = sl + (bias ? bias[ec] : 0.f);
-        key[j] = order_key((double)lf[j]);
-        if (e >= E) taken |= 1u << j;
+        const uint32_t u = __float_as_uint(lf[j] + 0.0f);
+        const uint32_t kf = (u >> 31) ? ~u : (u | 0x80000000u);
+        key[j] = e < E ? (kf & ~0x3FFu) | (uint32_t)(1023 - e) : 0u;
     }
-    uint64_t kth = 0;
-    for (int r = 0; r < k; ++r) {
-        uint64_t bk = 0;
-        int be = 0x7FFFFFFF;
 #pragma unroll
-        for (int j = 0; j < J; ++j)
-            if (!((taken >> j) & 1u) && ahead(key[j], lane + 64 * j, bk, be)) { bk = key[j]; be = lane + 64 * j; }
-        wave_argmax(bk, be);
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        kth = bk;
+    for (int i = 1; i < J; ++i)
+#pragma unroll
+        for (int j = i; j > 0; --j) {
+            const uint32_t a = key[j - 1], b = key[j];
+            key[j - 1] = a > b ? a : b;
+            key[j] = a > b ? b : a;
+        }
+    uint32_t kth = 0;
+    for (int r = 0; r < k; ++r) {
+        kth = wave_max_u32(key[0]);
+        const uint32_t m = key[0] == kth ? ~0u : 0u;  // the owner drops its head
+#pragma unroll
+        for (int j = 0; j + 1 < J; ++j) key[j] = (key[j + 1] & m) | (key[j] & ~m);
+        key[J - 1] &= ~m;
     }
+    const uint32_t kb = kth & ~0x3FFu;
+    const float kth_v = __uint_as_float((kb >> 31) ? (kb & 0x7FFFFFFFu) : ~kb);
     const double tol = ldexp((double)H, -21) * (xnorm * (double)rstat[0] + (double)rstat[1]);
-    const double thr = key_value(kth) - 2.0 * tol;
+    const double thr = (double)kth_v - 2.0 * tol;
     // candidate list, ascending expert id
     int nc = 0;
 #pragma unroll
