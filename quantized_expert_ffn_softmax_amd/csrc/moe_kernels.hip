@@ -704,7 +704,7 @@ constexpr int kRing = 8;  // chunks in flight per wave beyond the one being mult
 // row tiles; the fragments go to LDS as soon as they arrive and every further
 // chunk is requested as one is consumed.  K = F fits one pass (nch <= NC).
 // Output: part[a][t][row].
-template <int FMT, int NC, int FPER, int NV, int RP>
+template <int FMT, int NC, int FPER, int NV, int RP, int RING>
 __global__ __launch_bounds__(512 / RP) void k_down_decode(int T, const uint8_t* slots, Geom g,
                                                           const int32_t* __restrict__ nact,
                                                           const int32_t* __restrict__ act, int maxA,
@@ -738,10 +738,12 @@ __global__ __launch_bounds__(512 / RP) void k_down_decode(int T, const uint8_t* 
     f32x4_t acc[RP], corr[RP];
 #pragma unroll
     for (int r = 0; r < RP; ++r) acc[r] = corr[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // ring depth: kRing chunks; 2 for the 16-chunk case (F = 2048), which keeps
-    // the kernel at 58 VGPRs, i.e. 8 waves per SIMD, so that a DeepSeek-shaped
-    // call's whole grid is resident at once (measured faster than a ring of 4)
-    constexpr int R = NC < kRing ? NC : (NC > 8 ? 2 : kRing);
+    // ring depth RING (chosen by the launcher): all chunks for K of up to 8
+    // chunks; for the 16-chunk case (F = 2048) the deepest ring that keeps the
+    // whole grid resident at once: 2 (58 VGPRs, 8 waves per SIMD) for a
+    // DeepSeek-shaped window of 4 tokens, 8 when the grid fills at most two
+    // waves per SIMD (a window of 1)
+    constexpr int R = RING;
     uint32_t cw[R][RP][CWN];
     u32x2_t sc[R][RP];
     float s0[R], s1[R];
@@ -815,16 +817,30 @@ __global__ __launch_bounds__(512 / RP) void k_down_decode(int T, const uint8_t* 
     }
 }
 
-template <int FMT, int NC, int FPER, int NV>
-hipError_t launch_down_v(int T, const uint8_t* slots, const Geom& g, RouteBufs rb, DecodeBufs db, dim3 grid, int lds,
+template <int FMT, int NC, int FPER, int NV, int RING>
+hipError_t launch_down_r(int T, const uint8_t* slots, const Geom& g, RouteBufs rb, DecodeBufs db, dim3 grid, int lds,
                          int maxA, const Launch& lc) {
     constexpr int RP = FMT == 1 ? 1 : 2;  // row tiles per wave
     static int granted = 64 * 1024;
-    hipError_t e = ensure_lds(k_down_decode<FMT, NC, FPER, NV, RP>, lds, granted);
+    hipError_t e = ensure_lds(k_down_decode<FMT, NC, FPER, NV, RP, RING>, lds, granted);
     if (e != hipSuccess) return e;
-    launch(k_down_decode<FMT, NC, FPER, NV, RP>, grid, dim3(512 / RP), lds, lc, T, slots, g, rb.nact, rb.act, maxA,
-           db.afrag, db.spart, db.part);
+    launch(k_down_decode<FMT, NC, FPER, NV, RP, RING>, grid, dim3(512 / RP), lds, lc, T, slots, g, rb.nact, rb.act,
+           maxA, db.afrag, db.spart, db.part);
     return hipGetLastError();
+}
+
+template <int FMT, int NC, int FPER, int NV>
+hipError_t launch_down_v(int T, const uint8_t* slots, const Geom& g, RouteBufs rb, DecodeBufs db, dim3 grid, int lds,
+                         int maxA, const Launch& lc) {
+    if constexpr (NC <= 8) {
+        return launch_down_r<FMT, NC, FPER, NV, NC < kRing ? NC : kRing>(T, slots, g, rb, db, grid, lds, maxA, lc);
+    } else {
+        // waves per SIMD if the whole grid is resident (1024 SIMDs)
+        const int64_t waves = (int64_t)grid.x * grid.y * (FMT == 1 ? 8 : 4);
+        if (waves <= 2 * 1024) return launch_down_r<FMT, NC, FPER, NV, 8>(T, slots, g, rb, db, grid, lds, maxA, lc);
+        if (waves <= 4 * 1024) return launch_down_r<FMT, NC, FPER, NV, 4>(T, slots, g, rb, db, grid, lds, maxA, lc);
+        return launch_down_r<FMT, NC, FPER, NV, 2>(T, slots, g, rb, db, grid, lds, maxA, lc);
+    }
 }
 
 template <int FMT, int NC, int FPER>
