@@ -83,12 +83,14 @@ def test_raw_codes_cover_every_code_value(torch_cuda, cfg):
 
 
 def test_c4_deepseek_layer_with_shared_expert(torch_cuda):
-    """One layer of the 256+1-expert q4b32 shape at windows 1, 4, 8."""
+    """One layer of the 256+1-expert q4b32 shape at windows 1 to 4 and 8 (the
+    down projection's ring of in-flight chunks is 8 at a window of 1, 4 at 2,
+    and 2 from 3 on)."""
     from quantized_expert_ffn_softmax_amd import MoEContext
     cfg = C4
     with MoEContext.from_config(cfg, n_layers=1) as ctx:
         W, b, ex = load_layer(ctx, cfg, 2, 0)
-        for T in (1, 4, 8):
+        for T in (1, 2, 3, 4, 8):
             _check_layer(ctx, cfg, 2, 0, T, T, W, b, ex, f"C4/T{T}")
 
 
