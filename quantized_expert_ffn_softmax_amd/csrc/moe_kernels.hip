@@ -700,7 +700,7 @@ constexpr int kRing = 8;  // chunks in flight per wave beyond the one being mult
 // 2 (t / 4), v lo in the row after, so a lane's result registers 0, 1 hold
 // token lane / 16 and 2, 3 token lane / 16 + 4; NV = 2 for T <= 4 skips the
 // latter and stages the compact 32-lane fragments: the lanes of the zero rows
-// take a zero operand), then each wave requests the first kRing chunks of its
+// take a zero operand), then each wave requests the first RING chunks of its
 // row tiles; the fragments go to LDS as soon as they arrive and every further
 // chunk is requested as one is consumed.  K = F fits one pass (nch <= NC).
 // Output: part[a][t][row].
@@ -835,7 +835,8 @@ hipError_t launch_down_v(int T, const uint8_t* slots, const Geom& g, RouteBufs r
     if constexpr (NC <= 8) {
         return launch_down_r<FMT, NC, FPER, NV, NC < kRing ? NC : kRing>(T, slots, g, rb, db, grid, lds, maxA, lc);
     } else {
-        // waves per SIMD if the whole grid is resident (1024 SIMDs)
+        // the grid's waves against the chip's 1024 SIMDs: a ring of 8 while every
+        // wave fits at two per SIMD, of 4 at four per SIMD, else 2
         const int64_t waves = (int64_t)grid.x * grid.y * (FMT == 1 ? 8 : 4);
         if (waves <= 2 * 1024) return launch_down_r<FMT, NC, FPER, NV, 8>(T, slots, g, rb, db, grid, lds, maxA, lc);
         if (waves <= 4 * 1024) return launch_down_r<FMT, NC, FPER, NV, 4>(T, slots, g, rb, db, grid, lds, maxA, lc);
