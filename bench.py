@@ -488,9 +488,20 @@ def summarize_pmc(args):
 
 
 def kernel_sha(source="moe_kernels.hip"):
+    """Hash of the code a kernel is built from: the source and the two device headers it includes, with
+    comments, blank lines and trailing spaces removed, so that a comment edit keeps counters valid while
+    any change to the code drops them."""
     import hashlib
-    with open(os.path.join(ROOT, "quantized_expert_ffn_softmax_amd", "csrc", source), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    import re
+    h = hashlib.sha256()
+    for name in (source, "moe_device.h", "moe_internal.h"):
+        with open(os.path.join(ROOT, "quantized_expert_ffn_softmax_amd", "csrc", name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+        h.update(name.encode() + b"\0" + code.encode() + b"\0")
+    return h.hexdigest()[:16]
 
 
 def host_cpu():
