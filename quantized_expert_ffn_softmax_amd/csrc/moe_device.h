@@ -165,6 +165,56 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return v;
 }
 
+// Wave sums of N values per lane at once (N = 1, 2, 4, 8), reduce-scatter
+// style: for each lane bit 5, 4, 3 (as many as log2 N) a lane keeps half of
+// its remaining values and adds the partner lane's copy of them, so the
+// exchanges shrink by half each time; the lanes left per value are then summed
+// with DPP (and the cross-row exchanges N < 4 still needs).  Lane l returns
+// the sum of value l >> (6 - log2 N) over all 64 lanes (every lane of that
+// group of 64 / N lanes holds it).  Fixed order: deterministic.
+constexpr int kDppRowRor8 = 0x128;  // row_ror:8 (lane l <-> l ^ 8 inside a row of 16)
+template <class V> __device__ __forceinline__ V xchg_lane(V v, int bit) {
+    if constexpr (sizeof(V) == 8) {
+        if (bit == 8) return dpp_f64<kDppRowRor8>(v);
+        return __shfl_xor(v, bit);
+    } else {
+        if (bit == 8) return __int_as_float(dpp<kDppRowRor8>(__float_as_int(v)));
+        return __shfl_xor(v, bit);
+    }
+}
+template <int N, class V> __device__ __forceinline__ V wave_sum_scatter(V (&a)[N], int lane) {
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8, "1, 2, 4 or 8 values");
+    int cnt = N;
+#pragma unroll
+    for (int bit = 32; bit >= 8 && bit * N > 32; bit >>= 1) {
+        const int half = cnt / 2;
+        const bool up = (lane & bit) != 0;
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            if (i < half) {
+                const V keep = up ? a[i + half] : a[i], send = up ? a[i] : a[i + half];
+                a[i] = keep + xchg_lane(send, bit);
+            }
+        }
+        cnt = half;
+    }
+    V v = a[0];
+    if constexpr (sizeof(V) == 8) {
+        v += dpp_f64<kDppXor1>(v);
+        v += dpp_f64<kDppXor2>(v);
+        v += dpp_f64<kDppHalfMirror>(v);
+        if constexpr (N <= 4) v += dpp_f64<kDppMirror>(v);
+    } else {
+        v += __int_as_float(dpp<kDppXor1>(__float_as_int(v)));
+        v += __int_as_float(dpp<kDppXor2>(__float_as_int(v)));
+        v += __int_as_float(dpp<kDppHalfMirror>(__float_as_int(v)));
+        if constexpr (N <= 4) v += __int_as_float(dpp<kDppMirror>(__float_as_int(v)));
+    }
+    if constexpr (N <= 2) v += __shfl_xor(v, 16);
+    if constexpr (N == 1) v += __shfl_xor(v, 32);
+    return v;
+}
+
 // Total order of doubles as unsigned keys (-0 folded into +0).
 __device__ __forceinline__ uint64_t order_key(double v) {
     const uint64_t u = (uint64_t)__double_as_longlong(v + 0.0);

@@ -201,7 +201,11 @@ __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restric
         for (int t = 0; t < TT; ++t)
             xv[j][t] = *reinterpret_cast<const u32x4_t*>(x + (int64_t)min(t, T - 1) * H + h0 + 8 * seg);
     }
+    // lane l ends the wave reductions below with token l >> TSH's sum
+    constexpr int TSH = TT == 1 ? 6 : TT == 2 ? 5 : TT == 4 ? 4 : 3;
+    const bool tlead = (lane & ((1 << TSH) - 1)) == 0;
     if constexpr (PRE) {
+        float ssv[TT];
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
             float ss = 0.f;
@@ -217,11 +221,10 @@ __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restric
                     }
                 }
             }
-            ss = row_sum_f32(ss);
-            ss += __shfl_xor(ss, 16);
-            ss += __shfl_xor(ss, 32);
-            if (lane == 0) s_ss[wave][t] = ss;
+            ssv[t] = ss;
         }
+        const float ssw = wave_sum_scatter<TT>(ssv, lane);
+        if (tlead) s_ss[wave][lane >> TSH] = ssw;
         __syncthreads();
         if ((int)threadIdx.x < TT) {
             const int t = threadIdx.x;
@@ -265,11 +268,8 @@ __global__ __launch_bounds__(256) void k_router_decode(const uint16_t* __restric
             }
         }
     }
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-        const double v = wave_sum_f64(acc[t]);
-        if (lane == 0) s_part[wave][t] = v;
-    }
+    const double accw = wave_sum_scatter<TT>(acc, lane);
+    if (tlead) s_part[wave][lane >> TSH] = accw;
     __syncthreads();
     if ((int)threadIdx.x < T) {
         const int t = threadIdx.x;
