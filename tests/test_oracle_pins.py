@@ -351,6 +351,25 @@ def test_layer_with_shared_expert_equals_brute_force():
     np.testing.assert_allclose(y, _dense_layer(cfg, x, W, b, ex), rtol=1e-11, atol=1e-15)
 
 
+def test_combine_with_arbitrary_routing_equals_dense():
+    """The combine step on its own, as the hash-routed tests call it: ids in
+    table order (not sorted, not the score top-k), weights that do not sum to
+    1, a shared expert; equal to numpy's dense sum over the decoded matrices."""
+    from moe_inputs.configs import MoEConfig
+    cfg = MoEConfig("tiny_combine", (3,), 96, 64, 7, 1, 3, 1, Q2B32, mi.BIAS_NONE, 0.0)
+    ex = mi.gen_experts(11, 0, 0, cfg.E + cfg.S, cfg.H, cfg.F, cfg.fmt)
+    x = mi.gen_x(11, 0, 3, cfg.H)
+    ids = np.array([[5, 0, 3], [6, 2, 1], [1, 4, 0]], dtype=np.int32)
+    w = np.array([[0.5, 0.25, 1.5], [1.0, -0.75, 0.125], [2.0, 0.0, 0.3]])
+    y = oracle.combine(x, cfg.H, cfg.F, cfg.E, cfg.S, cfg.k, cfg.fmt, ids, w, ex, cfg.expert_bytes)
+    nb = cfg.expert_bytes
+    mats = [oracle.expert_matrices(ex[e * nb:(e + 1) * nb], cfg.H, cfg.F, cfg.fmt) for e in range(cfg.E + 1)]
+    for t in range(3):
+        xd = oracle.bf16_to_f64(x[t])
+        ref = sum(w[t, j] * _dense_ffn(*mats[ids[t, j]], xd) for j in range(cfg.k)) + _dense_ffn(*mats[cfg.E], xd)
+        np.testing.assert_allclose(y[t], ref, rtol=1e-12, atol=1e-15)
+
+
 def test_residual_rounding_matches_torch():
     rng = np.random.default_rng(0)
     xb = mi.gen_x(1, 0, 2, 64)
