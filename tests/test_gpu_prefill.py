@@ -189,6 +189,16 @@ def test_prefill_chain_teacher_forced(torch_cuda):
         assert_y_close(bf16_dev_to_f64(y), y_ref, "prefill chain output")
 
 
+@pytest.mark.parametrize("cfg,T", [(PF_Q4_SHARED, 300), (PF_Q2, 600), (PF_ODD, 300)], ids=lambda v: getattr(v, "name", str(v)))
+def test_prefill_raw_codes_cover_every_code_value(torch_cuda, cfg, T):
+    """Uniform codes over the full range (0 and the maximum included) and
+    random-sign scales through the grouped GEMMs' in-register dequantisation."""
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    with MoEContext.from_config(cfg, max_tokens=T, n_layers=1) as ctx:
+        W, b, ex = load_layer(ctx, cfg, 9, 0, raw=True)
+        _check_full(ctx, cfg, 9, 0, 2, T, W, b, ex, f"{cfg.name}/raw/T{T}")
+
+
 def test_prefill_determinism_bitwise(torch_cuda):
     from quantized_expert_ffn_softmax_amd import MoEContext
     cfg = PF_Q2

@@ -100,6 +100,15 @@ def test_prefill_full_output(torch_cuda, cfg, T):
         _check_layer(ctx, cfg, 7, 0, 11, T, W, b, ex, f"{cfg.name}/prefill/T{T}")
 
 
+def test_prefill_raw_codes_cover_every_code_value(torch_cuda):
+    """Uniform 2-bit codes and random-sign 64-block scales through the grouped GEMMs."""
+    from quantized_expert_ffn_softmax_amd import MoEContext
+    for cfg, T in ((SMALL, 300), (ODD, 200)):
+        with MoEContext.from_config(cfg, max_tokens=T, n_layers=1) as ctx:
+            W, b, ex = load_layer(ctx, cfg, 9, 0, raw=True)
+            _check_layer(ctx, cfg, 9, 0, 12, T, W, b, ex, f"{cfg.name}/prefill/raw/T{T}")
+
+
 def test_short_chain_teacher_forced(torch_cuda):
     """Four Qwen-shaped q2b64 layers with the pre-norm and residual at window 4:
     per layer the routing matches the oracle on the GPU's own normalised input,
