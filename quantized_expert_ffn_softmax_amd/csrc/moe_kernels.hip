@@ -332,7 +332,7 @@ hipError_t launch_router_decode(const uint16_t* x, int T, const uint16_t* Wr, co
 // sort uses one bitmask of tokens per expert: the pairs of a token have
 // distinct experts, so the rank of pair (t, j) inside the group of expert e is
 // the number of tokens t' < t that chose e, and the group size is popc(mask).
-template <int J>
+template <int J, int R2>
 __global__ __launch_bounds__(256) void k_topk_sort(int T, int E, int k, int S, RouteBufs rb,
                                                    const int32_t* __restrict__ tab, const int32_t* __restrict__ tok,
                                                    int vocab, int32_t* __restrict__ trace_ids,
@@ -348,11 +348,11 @@ __global__ __launch_bounds__(256) void k_topk_sort(int T, int E, int k, int S, R
     __shared__ double s_lg[4][64 * J];  // a wave's logits of its current token
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int P = T * k;
-    // logits of this wave's tokens (t = wave, wave + 4) are requested first
-    // (unconditional loads with clamped indices: all of them are in flight together)
-    double raw[2][J];
+    // logits of this wave's tokens (t = wave, and wave + 4 when R2 = 2, i.e. T > 4) are
+    // requested first (unconditional loads with clamped indices: all of them are in flight together)
+    double raw[R2][J];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < R2; ++r) {
         const int t = min(wave + 4 * r, T - 1);
 #pragma unroll
         for (int j = 0; j < J; ++j) raw[r][j] = rb.logits[(int64_t)t * E + min(lane + 64 * j, E - 1)];
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256) void k_topk_sort(int T, int E, int k, int S, R
     __syncthreads();
 
 #pragma unroll
-    for (int r2 = 0; r2 < 2; ++r2) {
+    for (int r2 = 0; r2 < R2; ++r2) {
         const int t = wave + 4 * r2;
         if (t >= T) break;
         int my_e = 0;
@@ -469,12 +469,17 @@ __global__ __launch_bounds__(256) void k_topk_sort(int T, int E, int k, int S, R
 
 hipError_t launch_topk_sort_decode(int T, const Geom& g, RouteBufs rb, const int32_t* tab, const int32_t* tok, int vocab,
                                    int32_t* trace_ids, float* trace_w, const Launch& lc) {
-    if (g.E <= 256)
-        launch(k_topk_sort<4>, dim3(1), dim3(256), 0, lc, T, g.E, g.k, g.S, rb, tab, tok, vocab, trace_ids, trace_w);
-    else if (g.E <= 512)
-        launch(k_topk_sort<8>, dim3(1), dim3(256), 0, lc, T, g.E, g.k, g.S, rb, tab, tok, vocab, trace_ids, trace_w);
-    else
-        launch(k_topk_sort<16>, dim3(1), dim3(256), 0, lc, T, g.E, g.k, g.S, rb, tab, tok, vocab, trace_ids, trace_w);
+    // R2 = 1 for windows of up to 4 tokens: one token per wave, no second round of logit loads
+#define MOE_TOPK_CASE(J, R2) \
+    launch(k_topk_sort<J, R2>, dim3(1), dim3(256), 0, lc, T, g.E, g.k, g.S, rb, tab, tok, vocab, trace_ids, trace_w)
+    if (g.E <= 256) {
+        if (T <= 4) MOE_TOPK_CASE(4, 1); else MOE_TOPK_CASE(4, 2);
+    } else if (g.E <= 512) {
+        if (T <= 4) MOE_TOPK_CASE(8, 1); else MOE_TOPK_CASE(8, 2);
+    } else {
+        if (T <= 4) MOE_TOPK_CASE(16, 1); else MOE_TOPK_CASE(16, 2);
+    }
+#undef MOE_TOPK_CASE
     return hipGetLastError();
 }
 
@@ -958,7 +963,8 @@ __global__ __launch_bounds__(256) void k_combine_decode(const uint16_t* __restri
 
 hipError_t launch_combine_decode(const uint16_t* x, int T, const Geom& g, RouteBufs rb, DecodeBufs db, uint16_t* y,
                                  int residual, const Launch& lc) {
-    launch(k_combine_decode, dim3((T * g.H + 255) / 256), dim3(256), 0, lc, x, T, g.H, rb.nact, db.part, y,
+    // one-wave workgroups: the partial rows' requests spread over four times as many CUs
+    launch(k_combine_decode, dim3((T * g.H + 63) / 64), dim3(64), 0, lc, x, T, g.H, rb.nact, db.part, y,
                        residual);
     return hipGetLastError();
 }
