@@ -4,6 +4,8 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -337,11 +339,30 @@ __device__ __forceinline__ bool wave_topk_fast(const double* raw, int E, int k, 
     return true;
 }
 
-// Raise a kernel's dynamic LDS limit when a launch needs more than the default.
-template <class K> hipError_t ensure_lds(K kernel, int bytes, int& granted) {
-    if (bytes <= granted) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e == hipSuccess) granted = bytes;
+// Raise a kernel's dynamic LDS limit when a launch needs more than the
+// default 64 KiB.  The limit belongs to the kernel on each device, so what has
+// been granted is kept per device ordinal (ordinals from kLdsDevices on set the
+// attribute on every launch that needs it), and a mutex orders the updates of
+// host threads that launch at the same time.  One LdsGrant per kernel.
+constexpr int kLdsDefault = 64 * 1024;
+constexpr int kLdsDevices = 64;
+struct LdsGrant {
+    std::mutex mu;
+    int bytes[kLdsDevices];
+    LdsGrant() {
+        for (int& b : bytes) b = kLdsDefault;
+    }
+};
+template <class K> hipError_t ensure_lds(K kernel, int bytes, LdsGrant& granted) {
+    if (bytes <= kLdsDefault) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool tracked = dev >= 0 && dev < kLdsDevices;
+    std::lock_guard<std::mutex> lk(granted.mu);
+    if (tracked && bytes <= granted.bytes[dev]) return hipSuccess;
+    e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && tracked) granted.bytes[dev] = bytes;
     return e;
 }
 

@@ -646,7 +646,7 @@ __global__ __launch_bounds__(256) void k_gateup_decode(const uint16_t* __restric
 template <int FMT, int NC, int XPER, int R>
 hipError_t launch_gateup_r(const uint16_t* x, int T, const uint8_t* slots, const Geom& g, RouteBufs rb,
                            DecodeBufs db, int maxA_T, int maxA, const Launch& lc) {
-    static int granted = 64 * 1024;
+    static LdsGrant granted;
     const int xbytes = T * (g.H + 8) * 2 + 16;  // + the dummy slot of the staging stores
     const int lds = xbytes > 3 * 4 * 64 * 16 ? xbytes : 3 * 4 * 64 * 16;
     hipError_t e = ensure_lds(k_gateup_decode<FMT, NC, XPER, R>, lds, granted);
@@ -826,7 +826,7 @@ template <int FMT, int NC, int FPER, int NV, int RING>
 hipError_t launch_down_r(int T, const uint8_t* slots, const Geom& g, RouteBufs rb, DecodeBufs db, dim3 grid, int lds,
                          int maxA, const Launch& lc) {
     constexpr int RP = FMT == 1 ? 1 : 2;  // row tiles per wave
-    static int granted = 64 * 1024;
+    static LdsGrant granted;
     hipError_t e = ensure_lds(k_down_decode<FMT, NC, FPER, NV, RP, RING>, lds, granted);
     if (e != hipSuccess) return e;
     launch(k_down_decode<FMT, NC, FPER, NV, RP, RING>, grid, dim3(512 / RP), lds, lc, T, slots, g, rb.nact, rb.act,

@@ -995,7 +995,7 @@ hipError_t launch_router_stats(const uint16_t* Wr, const float* bias, int E, int
 hipError_t launch_pf_router(const uint16_t* x, int T, const uint16_t* Wr, const float* bias, const Geom& g,
                             PrefillBufs pb, const Launch& lc) {
     (void)bias;  // added by the top-k kernel
-    static int granted = 64 * 1024;
+    static LdsGrant granted;
     hipError_t e = ensure_lds(k_pf_router, kPrLds, granted);
     if (e != hipSuccess) return e;
     const int ks = pf_router_splits(T, g.E, g.H);
@@ -1046,7 +1046,7 @@ hipError_t launch_pf_scatter(int T, const Geom& g, PrefillBufs pb, const Launch&
 template <int FMT, int MODE>
 static hipError_t launch_gemm(const uint16_t* x, const uint8_t* slots, const Geom& g, PrefillBufs pb,
                               const Launch& lc) {
-    static int granted = 64 * 1024;
+    static LdsGrant granted;
     hipError_t e = ensure_lds(k_pf_gemm<FMT, MODE>, kGemmLds, granted);
     if (e != hipSuccess) return e;
     const int ntn = MODE == 1 ? (g.F + 127) / 128 : (g.H + 255) / 256;
