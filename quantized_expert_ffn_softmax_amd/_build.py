@@ -23,7 +23,10 @@ FLAGS = [
 
 def build(verbose: bool = False) -> str:
     """Compiles every source to an object in parallel, then links libmoe.so."""
-    srcs = [os.path.join(HERE, s) for s in SOURCES if os.path.exists(os.path.join(HERE, s))]
+    srcs = [os.path.join(HERE, s) for s in SOURCES]
+    missing = [s for s in srcs if not os.path.exists(s)]
+    if missing:
+        raise RuntimeError(f"HIP sources missing: {missing}")
     inc = ["-I", os.path.join(os.path.dirname(HERE), "include")]
     objs, procs = [], []
     for src in srcs:
