@@ -19,7 +19,8 @@
 //   k_down_decode     per (active expert, 128-row group of H): down GEMV with
 //                     the expert's operand staged once in LDS; stores one
 //                     partial row block per expert
-//   k_combine_decode  sums the experts in ascending active order (no atomics,
+//   k_combine_decode  one-wave workgroups, a thread per output element: sums
+//                     the experts in ascending active order (no atomics,
 //                     deterministic), adds the residual, writes bf16
 //
 // Method references (pages): sparse top-k routing with a shared expert and
@@ -325,7 +326,8 @@ hipError_t launch_router_decode(const uint16_t* x, int T, const uint16_t* Wr, co
 }
 
 // ---------------------------------------------------------------- top-k + sort
-// One workgroup of 4 waves; wave w routes tokens w and w+4 (selection on
+// One workgroup of 4 waves; wave w routes token w, and token w+4 when R2 = 2
+// (windows of 5 to 8 tokens; R2 = 1 skips that round's logit loads) (selection on
 // 32-bit keys of the fp32-rounded logit and the id, with an exact fp64
 // fallback when two of the k+1 best keys agree above the id bits, see
 // wave_topk_fast; weights from the fp64 logits).  The counting
