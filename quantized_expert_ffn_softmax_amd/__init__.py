@@ -95,12 +95,19 @@ def _check(status):
         raise MoEError(status, lib().moe_last_error().decode(errors="replace"))
 
 
-def _dptr(t):
-    """Device address of a torch tensor (or None)."""
+def _dptr(t, itemsize=None, name="tensor"):
+    """Device address of a contiguous GPU tensor (or None).  The library reads
+    and writes these addresses from its kernels, so a host tensor, or elements
+    of another width than the call's layout (2 bytes: bf16 activations and
+    router weights; 4 bytes: int32 ids and fp32 weights), is rejected here."""
     if t is None:
         return None
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
-        raise ValueError("tensors passed to libmoe must be contiguous")
+        raise ValueError(f"{name} must be contiguous")
+    if itemsize is not None and t.element_size() != itemsize:
+        raise ValueError(f"{name} must have {itemsize}-byte elements, got {t.element_size()}")
     return t.data_ptr()
 
 
@@ -142,22 +149,24 @@ def moe_load_experts(ctx, layer, router_w=None, router_bias=None, experts=None, 
 
 
 def moe_route(ctx, layer, x, T, ids, w, offsets=None, perm=None, stream=None, token_ids=None):
-    _check(lib().moe_route(ctx, layer, _dptr(x), T, _dptr(token_ids), _dptr(ids), _dptr(w), _dptr(offsets),
-                           _dptr(perm), _stream(stream)))
+    _check(lib().moe_route(ctx, layer, _dptr(x, 2, "x"), T, _dptr(token_ids, 4, "token_ids"), _dptr(ids, 4, "ids"),
+                           _dptr(w, 4, "w"), _dptr(offsets, 4, "offsets"), _dptr(perm, 4, "perm"), _stream(stream)))
 
 
 def moe_route_static(x, T, hidden, n_experts, top_k, router_w, router_bias, ids, w, offsets=None, perm=None,
                      stream=None):
     """Decode-window routing on device router weights with the library's static scratch (no context, no
     allocation)."""
-    _check(lib().moe_route_static(_dptr(x), T, hidden, n_experts, top_k, _dptr(router_w), _dptr(router_bias),
-                                  _dptr(ids), _dptr(w), _dptr(offsets), _dptr(perm), _stream(stream)))
+    _check(lib().moe_route_static(_dptr(x, 2, "x"), T, hidden, n_experts, top_k, _dptr(router_w, 2, "router_w"),
+                                  _dptr(router_bias, 4, "router_bias"), _dptr(ids, 4, "ids"), _dptr(w, 4, "w"),
+                                  _dptr(offsets, 4, "offsets"), _dptr(perm, 4, "perm"), _stream(stream)))
 
 
 def moe_forward(ctx, x, y, T, layer_begin=0, layer_count=1, flags=0, trace_x=None, trace_ids=None, trace_w=None,
                 stream=None, token_ids=None):
-    a = moe_fwd_args(layer_begin, layer_count, T, flags, _dptr(x), _dptr(y), _dptr(trace_x), _dptr(trace_ids),
-                     _dptr(trace_w), _dptr(token_ids))
+    a = moe_fwd_args(layer_begin, layer_count, T, flags, _dptr(x, 2, "x"), _dptr(y, 2, "y"),
+                     _dptr(trace_x, 2, "trace_x"), _dptr(trace_ids, 4, "trace_ids"), _dptr(trace_w, 4, "trace_w"),
+                     _dptr(token_ids, 4, "token_ids"))
     _check(lib().moe_forward(ctx, ctypes.byref(a), _stream(stream)))
 
 
@@ -201,9 +210,20 @@ class MoEContext:
         count = 0 if experts is None else experts.nbytes // self.expert_bytes
         moe_load_experts(self.handle, layer, router_w, router_bias, experts, expert_begin, count, tid2eid)
 
+    def _rows(self, x, token_ids=None, y=None):
+        """T of an activation tensor [T, H]; y and token_ids must match it."""
+        if x.dim() != 2 or x.shape[1] != self.H:
+            raise ValueError(f"x must be [T, {self.H}], got {tuple(x.shape)}")
+        T = x.shape[0]
+        if y is not None and tuple(y.shape) != tuple(x.shape):
+            raise ValueError(f"y must be {tuple(x.shape)}, got {tuple(y.shape)}")
+        if token_ids is not None and token_ids.numel() < T:
+            raise ValueError(f"token_ids holds {token_ids.numel()} ids for {T} tokens")
+        return T
+
     def route(self, layer, x, stream=None, token_ids=None):
         import torch
-        T = x.shape[0]
+        T = self._rows(x, token_ids)
         dev = x.device
         ids = torch.empty((T, self.k), dtype=torch.int32, device=dev)
         w = torch.empty((T, self.k), dtype=torch.float32, device=dev)
@@ -215,7 +235,7 @@ class MoEContext:
     def forward(self, x, layer_begin=0, layer_count=1, residual=False, trace=False, y=None, stream=None,
                 profile=False, prenorm=False, token_ids=None):
         import torch
-        T = x.shape[0]
+        T = self._rows(x, token_ids, y)
         if y is None:
             y = torch.empty_like(x)
         tx = tid = tw = None

@@ -110,3 +110,48 @@ def test_static_route_argument_checks():
     assert f(None, 4, 256, 16, 2, None, None, None, None, None, None, None) == moe.MOE_EINVAL  # NULL pointers
     assert b"required" in lib.moe_last_error()
     assert f(None, 0, 4096, 1024, 16, None, None, None, None, None, None, None) == moe.MOE_OK  # T = 0: no-op
+
+
+def test_binding_rejects_tensors_the_kernels_cannot_read():
+    """Host tensors, non-contiguous views and elements of the wrong width are
+    refused before any call reaches the library; activations must be [T, H]."""
+    import torch
+    x = torch.zeros((4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.moe_forward(None, x, x, 4)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.moe_route(None, 0, x, 4, None, None)
+
+    class Dev:  # stands for a device tensor: the checks read only these attributes
+        is_cuda = True
+
+        def __init__(self, size, contiguous=True):
+            self.size, self.contiguous = size, contiguous
+
+        def is_contiguous(self):
+            return self.contiguous
+
+        def element_size(self):
+            return self.size
+
+        def data_ptr(self):
+            return 0x1000
+
+    assert moe._dptr(None, 2, "x") is None
+    assert moe._dptr(Dev(2), 2, "x") == 0x1000
+    with pytest.raises(ValueError, match="2-byte"):
+        moe._dptr(Dev(4), 2, "x")
+    with pytest.raises(ValueError, match="contiguous"):
+        moe._dptr(Dev(2, contiguous=False), 2, "x")
+    ctx = moe.MoEContext.__new__(moe.MoEContext)
+    ctx.H, ctx.handle = 64, None
+    assert ctx._rows(x) == 4
+    assert ctx._rows(x, torch.zeros(4, dtype=torch.int32), torch.zeros_like(x)) == 4
+    with pytest.raises(ValueError, match=r"\[T, 64\]"):
+        ctx._rows(torch.zeros((4, 32), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match=r"\[T, 64\]"):
+        ctx._rows(torch.zeros(256, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="y must be"):
+        ctx._rows(x, y=torch.zeros((3, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="token_ids"):
+        ctx._rows(x, torch.zeros(3, dtype=torch.int32))
